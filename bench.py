@@ -1,0 +1,227 @@
+"""Benchmark of the SplitZip exponent codec on one MI355X.
+
+One step = compress + decompress of the whole workload (every step of the
+hot path: split, code map, nibble/sign|mantissa packing, escape compaction and
+device-wide offset scan, header; then LUT decode, recombine, escape overwrite).
+Inputs are resident in HBM before the timed region.  Prints one JSON line.
+
+Default workload: Llama-3-8B-shaped prefill KV cache, BF16
+[32 layers, 2, 8192 tokens, 8 kv heads, 128] = 1 GiB, per-layer codebooks.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "lossless_kv_cache_splitzip_amd", "csrc", "splitzip.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != source_digest():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(wl_name: str, budget_s: float):
+    """The oracle as it stands (single-threaded C), timed on whole layers of
+    the same workload, one after another, until about budget_s seconds of
+    CPU work (at least one layer).  Each layer is compressed with its own
+    codebook and decompressed again."""
+    import numpy as np
+
+    import kvsynth
+    import oracle
+
+    spec = kvsynth.SPECS[wl_name]
+    dtype = spec.dtype
+    done = raw = 0
+    t_enc = t_dec = 0.0
+    while done < spec.layers and (t_enc + t_dec) < budget_s:
+        x, c = kvsynth.layer(wl_name, done, device="cpu")
+        x = kvsynth.to_numpy_bits(x)
+        cb = oracle.calibrate(dtype, kvsynth.to_numpy_bits(c))
+        t0 = time.perf_counter()
+        s = oracle.compress(dtype, x, cb)
+        t1 = time.perf_counter()
+        y = oracle.decompress(s, dtype, x.size)
+        t2 = time.perf_counter()
+        assert np.array_equal(y, x)
+        t_enc += t1 - t0
+        t_dec += t2 - t1
+        raw += x.nbytes
+        done += 1
+    return {
+        "value": raw / (t_enc + t_dec) / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {spec.layers} layers ({raw / 2**20:.0f} MiB raw) of the same workload, "
+                  f"compress + decompress, one codebook per layer, one thread",
+        "encode_GBps": raw / t_enc / 1e9,
+        "decode_GBps": raw / t_dec / 1e9,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b_kv_bf16")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this codec benchmark runs on one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kvsynth
+    import lossless_kv_cache_splitzip_amd as sz
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {args.workload} on {torch.cuda.get_device_name(dev)}")
+    wl = kvsynth.make(args.workload, device=dev)
+    dtype = wl.spec.dtype
+    cbs = np.stack([sz.splitzip_calibrate(dtype, kvsynth.to_numpy_bits(c)) for c in wl.calib])
+    seg = wl.segment_elems if cbs.shape[0] > 1 else 0
+    n = wl.n
+    raw = wl.raw_bytes
+    cap = sz.splitzip_max_compressed_size(dtype, n, cbs.shape[0])
+    out = torch.empty(cap, dtype=torch.uint8, device=dev)
+    out_bytes = torch.zeros(1, dtype=torch.int64, device=dev)
+    dec = torch.empty_like(wl.data)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sz.compress(wl.data, cbs, seg, out=out, out_bytes=out_bytes, stream=stream)
+        e_mid.record(stream)
+        sz.decompress(out, n, dtype, out=dec, status=status, in_bytes=cap, stream=stream)
+
+    # correctness of the timed configuration
+    e_mid = torch.cuda.Event(enable_timing=True)
+    step()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0 and torch.equal(dec.view(torch.uint8), wl.data.view(torch.uint8)), \
+        "round trip failed"
+    stream_bytes = int(out_bytes.item())
+    n_esc = int(np.frombuffer(out[16:24].cpu().numpy().tobytes(), "<u8")[0])
+    log(f"[bench] n={n} codebooks={cbs.shape[0]} stream={stream_bytes} escapes={n_esc} "
+        f"ratio={raw / stream_bytes:.4f}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b, c in ev:
+        a.record(stream)
+        e_mid = b
+        step()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    dec_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, encode {enc_ms:.3f} ms, decode {dec_ms:.3f} ms")
+
+    # measured device-to-device copy ceiling (read + write bytes / time)
+    cp_src = wl.data.view(torch.uint8)
+    cp_dst = torch.empty_like(cp_src)
+    for _ in range(3):
+        cp_dst.copy_(cp_src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(20):
+        cp_dst.copy_(cp_src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * cp_src.numel() * 20 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del cp_dst
+
+    elem = 2 if dtype == kvsynth.BF16 else 1
+    dense_out = (n + 1) // 2 + (n if dtype == kvsynth.BF16 else 3 * ((n + 7) // 8))
+    alg_enc = raw + dense_out + 3 * n_esc          # read input, write codes + sign|mantissa + escapes
+    alg_dec = dense_out + 3 * n_esc + raw          # read codes + sign|mantissa + escapes, write values
+    enc_gbps = alg_enc / (enc_ms / 1e3) / 1e9
+    dec_gbps = alg_dec / (dec_ms / 1e3) / 1e9
+    kname = "encode_bf16_kernel" if dtype == kvsynth.BF16 else "encode_e5m2_kernel"
+    dname = "decode_bf16_kernel" if dtype == kvsynth.BF16 else "decode_e5m2_kernel"
+    cpu = cpu_baseline(args.workload, args.cpu_budget) if args.cpu_budget > 0 else None
+
+    line = {
+        "metric": "encode & decode GB/s of raw BF16 KV, compression ratio, % of HBM roofline",
+        "value": raw / (ms_per_step / 1e3) / 1e9,
+        "unit": "GB/s (raw bytes per compress+decompress round trip)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16" if dtype == kvsynth.BF16 else "u8",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "elements": n, "raw_bytes": raw,
+                   "shape": [wl.spec.layers, 2, wl.spec.tokens, wl.spec.heads, wl.spec.head_dim],
+                   "element_type": "bf16" if dtype == kvsynth.BF16 else "fp8_e5m2",
+                   "codebooks": int(cbs.shape[0])},
+        "encode_GBps": raw / (enc_ms / 1e3) / 1e9,
+        "decode_GBps": raw / (dec_ms / 1e3) / 1e9,
+        "encode_ms": enc_ms,
+        "decode_ms": dec_ms,
+        "compression_ratio": raw / stream_bytes,
+        "escape_rate": n_esc / n,
+        "memcpy_d2d_GBps": copy_gbps,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": enc_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": enc_gbps / HBM_PEAK_GBPS, "frac_of_memcpy": enc_gbps / copy_gbps,
+                     "traffic": counter_traffic(kname, args.workload), "algorithmic_bytes": alg_enc},
+        "roofline_decode": {"bound": "hbm", "kernel": dname, "achieved": dec_gbps, "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": dec_gbps / HBM_PEAK_GBPS,
+                            "frac_of_memcpy": dec_gbps / copy_gbps,
+                            "traffic": counter_traffic(dname, args.workload), "algorithmic_bytes": alg_dec},
+        "cpu_baseline": cpu,
+        "pages_context": {"encode_GBps": 613.3, "decode_GBps": 2181.8, "hardware": "not stated in the pages"},
+        "kernel_source_sha256_16": source_digest(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

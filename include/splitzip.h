@@ -1,0 +1,133 @@
+/*
+ * splitzip.h -- C ABI of libsplitzip, a lossless exponent codec for BF16 and
+ * FP8 E5M2 KV-cache tensors on AMD Instinct MI355X (gfx950).
+ *
+ * The method is SplitZip ("SplitZip: Ultra Fast Lossless KV Compression for
+ * Disaggregated LLM Serving", arXiv 2605.01708v2).  Its pages state the
+ * problem this ABI serves: KV tensors must reach the decode side bit for bit,
+ * and the codec must plug into a serving stack without touching model
+ * execution (authors' abstract; Spanish technical summary, "Metodologia").
+ *
+ * Conventions for every call:
+ *   - extern "C", never throws, returns an int status (SPLITZIP_OK = 0 or a
+ *     negative SPLITZIP_E_* code); sizes are element or byte counts.
+ *   - "d_" pointers are device memory (hipMalloc'd, or any memory the GPU
+ *     can address); "h_" pointers are host memory.  The caller owns every
+ *     buffer.  No call allocates device or host memory.
+ *   - GPU work is enqueued on `stream` (NULL = the default stream) and is not
+ *     waited for.  Host-detectable argument errors return at once and enqueue
+ *     nothing.  A failed kernel launch returns SPLITZIP_E_HIP.
+ *   - Calls on different streams may run concurrently when their buffers are
+ *     disjoint; the library keeps no mutable global state.
+ *
+ * Stream format "SZ1" (little-endian; A(x) = x rounded up to a multiple of
+ * 256; n elements, C = ceil(n / 65536) chunks, K codebooks, E escapes):
+ *   0    u32 magic 0x00315A53        4  u16 version 1
+ *   6    u8  dtype                    7  u8  log2 chunk size = 16
+ *   8    u64 n                        16 u64 E
+ *   24   u64 total stream bytes S     32 u32 C      36 u32 K
+ *   40   u64 elements per segment (n when K == 1)
+ *   48   16 zero bytes
+ *   64          K codebooks of 16 bytes (byte k = exponent of 4-bit code k)
+ *   64 + 16K    C + 1 u64: escapes before chunk c (off[C] = E)
+ *   N0 = A(64 + 16K + 8(C + 1)): 4-bit codes, two per byte, even element in
+ *        the low nibble; an escaped element has code 0        (ceil(n/2) B)
+ *   N1 = N0 + A(ceil(n/2)): sign|mantissa
+ *        BF16: one byte per element, sign at bit 7, mantissa bits 6..0 (n B)
+ *        E5M2: 3 bits per element (sign << 2 | mantissa), 8 elements per 3
+ *              little-endian bytes, element j of a group at bits 3j  (3 ceil(n/8) B)
+ *   P  = N1 + A(sign|mantissa bytes): E escape records of 3 bytes
+ *        [position in chunk, low byte][high byte][raw exponent], in element order
+ *   S  = P + 3E.  All bytes between sections are zero.
+ * Chunk c is coded with codebook 0 when K == 1, else with codebook
+ * floor(65536 c / segment_elems).
+ */
+#ifndef SPLITZIP_H
+#define SPLITZIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  BF16: 1 sign, 8 exponent, 7 mantissa bits (English
+ * explainer, "1. The 'Note' Structure").  FP8 E5M2: 1 sign, 5 exponent,
+ * 2 mantissa bits (technical summary, "Contribuciones Clave" 4). */
+typedef enum { SPLITZIP_BF16 = 1, SPLITZIP_FP8_E5M2 = 2 } splitzip_dtype;
+
+enum {
+  SPLITZIP_OK = 0,
+  SPLITZIP_E_INVALID = -1,  /* bad argument: null/misaligned pointer, dtype, sizes, segments */
+  SPLITZIP_E_CAPACITY = -2, /* output buffer smaller than splitzip_max_compressed_size() */
+  SPLITZIP_E_CODEBOOK = -3, /* codebook entries repeated or out of range for the dtype */
+  SPLITZIP_E_CORRUPT = -4,  /* stream fails validation (reported through d_status) */
+  SPLITZIP_E_HIP = -5       /* a HIP launch failed */
+};
+
+/* Offline calibration (technical summary, "Metodologia / Codificacion de
+ * Longitud Fija" and "Optimizacion"; "Resultados / Calibracion"; abstract):
+ * histogram the exponents of n_elems host samples and return the 16 most
+ * frequent exponent values in codebook_out[0..15], most frequent first;
+ * equal counts go to the lower exponent; values never seen fill the
+ * remaining slots in ascending order, so the 16 entries are always distinct.
+ * host_samples: n_elems BF16 (uint16 bit patterns) or E5M2 (uint8) values in
+ * host memory; may be NULL only when n_elems == 0.  Synchronous, host only.
+ * Returns SPLITZIP_OK or SPLITZIP_E_INVALID. */
+int splitzip_calibrate(int dtype, const void* host_samples, size_t n_elems, uint8_t codebook_out[16]);
+
+/* Bytes the caller must provide as d_out of splitzip_compress for n_elems
+ * elements and n_codebooks codebooks: the largest possible stream (every
+ * element escaped) rounded up to 256, plus the encoder's scan workspace
+ * (256 + 8 ceil(n_elems / 8192) bytes).  Returns 0 for an invalid dtype,
+ * n_codebooks == 0 or n_elems > 2^40. */
+size_t splitzip_max_compressed_size(int dtype, size_t n_elems, uint32_t n_codebooks);
+
+/* Encode (technical summary, "Estrategia de Codificacion"; abstract; English
+ * explainer, "3. The SplitZip Strategy"): split every element into exponent
+ * and sign|mantissa, map the exponent through its chunk's codebook to a 4-bit
+ * code, and route exponents outside the codebook to the escape records.
+ *   d_in          n_elems elements (BF16 as uint16, E5M2 as uint8), 16-byte aligned.
+ *   h_codebooks   n_codebooks x 16 bytes, host memory, read before return.
+ *   segment_elems elements per codebook; ignored when n_codebooks == 1,
+ *                 else a non-zero multiple of 65536 with
+ *                 n_codebooks * segment_elems >= n_elems.
+ *   d_out         out_capacity bytes, 16-byte aligned; the stream is written
+ *                 at its start; bytes after the stream are the encoder's
+ *                 workspace and are overwritten.
+ *   d_out_bytes   optional (may be NULL): receives the stream size S, written
+ *                 by the GPU when the encode completes (device or pinned host
+ *                 memory, 8-byte aligned).
+ * The stream is byte-for-byte deterministic for given inputs.  d_in is not
+ * modified.  Returns SPLITZIP_OK, SPLITZIP_E_INVALID, SPLITZIP_E_CODEBOOK,
+ * SPLITZIP_E_CAPACITY or SPLITZIP_E_HIP. */
+int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks,
+                      uint32_t n_codebooks, size_t segment_elems, void* d_out, size_t out_capacity,
+                      uint64_t* d_out_bytes, hipStream_t stream);
+
+/* Decode (technical summary, "Estrategia de Decodificacion / Paralelismo"
+ * and "Correccion"; English explainer, "4. Why It's Fast"): map every 4-bit
+ * code through its codebook, recombine with the sign|mantissa bits, then
+ * overwrite the exponent of every escaped element with its raw value.
+ *   d_in      the stream (in_bytes >= its size S, 16-byte aligned).
+ *   dtype, n_elems must match the stream header.
+ *   d_out     n_elems elements, 16-byte aligned.
+ *   d_status  optional (may be NULL), device int32: set to SPLITZIP_OK, then
+ *             to SPLITZIP_E_CORRUPT if the GPU finds the stream invalid (bad
+ *             magic, version, dtype, n, sizes, codebook range, non-monotone
+ *             chunk offsets, escape positions out of range or out of order).
+ *             d_out is then unspecified.  Every read stays inside in_bytes.
+ * Returns SPLITZIP_OK, SPLITZIP_E_INVALID or SPLITZIP_E_HIP. */
+int splitzip_decompress(const void* d_in, size_t in_bytes, int dtype, size_t n_elems, void* d_out,
+                        int32_t* d_status, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* splitzip_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITZIP_H */

@@ -182,51 +182,68 @@ class Workload:
         return self.n * (2 if self.spec.dtype == BF16 else 1)
 
 
-def make(name: str, device="cpu", layers: int | None = None, tokens: int | None = None,
-         data: bool = True) -> Workload:
-    """Draw workload ``name``; ``layers``/``tokens`` shrink it for small tests
-    (the recipe and seeds stay the same)."""
-    base = SPECS[name]
-    spec = Spec(**{**base.__dict__})
+def _layer(spec: Spec, l: int, device, data: bool = True, calib: bool = True):
+    """Data and calibration sample of layer ``l`` of a workload."""
+    T, H, D = spec.tokens, spec.heads, spec.head_dim
+    seed = 1000 * spec.number + l
+    cseed = seed + 500000
+    x = c = None
+    if spec.kind == "gaussian":
+        sc = _channel_scales(seed, H, D, spec.sigma, spec.outlier_p, spec.outlier_f)
+        if data:
+            x = _gaussian_layer(seed, sc, T, H, D, spec.dtype, device)
+        if calib:
+            if spec.calib == "per_layer":
+                csc = sc
+            elif spec.calib == "rerun":
+                csc = _channel_scales(cseed, H, D, spec.sigma, spec.outlier_p, spec.outlier_f)
+            elif spec.calib == "sigma1":
+                csc = _channel_scales(cseed, H, D, 1.0, spec.outlier_p, spec.outlier_f)
+            else:
+                raise ValueError(spec.calib)
+            ct = spec.calib_tokens if spec.calib != "rerun" else T
+            c = _gaussian_layer(cseed, csc, ct, H, D, spec.dtype, device)
+    else:
+        n_l = spec.layer_elems
+        if data:
+            x = _edge_layer(spec.kind, seed, n_l, device)
+        if calib:
+            c = _edge_layer(spec.kind, cseed, min(n_l, 1 << 20), device)
+    return x, c
+
+
+def resize(name: str, layers: int | None = None, tokens: int | None = None) -> Spec:
+    """The recipe of workload ``name``, optionally with fewer layers/tokens."""
+    spec = Spec(**{**SPECS[name].__dict__})
     if layers is not None:
         spec.layers = layers
     if tokens is not None:
         spec.tokens = tokens
         if spec.kind == "gaussian":
             spec.calib_tokens = min(spec.calib_tokens, max(tokens, 16))
-    L, T, H, D = spec.layers, spec.tokens, spec.heads, spec.head_dim
+    return spec
+
+
+def make(name: str, device="cpu", layers: int | None = None, tokens: int | None = None) -> Workload:
+    """Draw workload ``name``; ``layers``/``tokens`` shrink it for small tests
+    (the recipe and seeds stay the same)."""
+    spec = resize(name, layers, tokens)
     parts = []
     calib = []
-    for l in range(L):
-        seed = 1000 * spec.number + l
-        cseed = seed + 500000
-        if spec.kind == "gaussian":
-            sc = _channel_scales(seed, H, D, spec.sigma, spec.outlier_p, spec.outlier_f)
-            if data:
-                parts.append(_gaussian_layer(seed, sc, T, H, D, spec.dtype, device))
-            if spec.per_layer_codebooks or l == 0:
-                if spec.calib == "per_layer":
-                    csc = sc
-                elif spec.calib == "rerun":
-                    csc = _channel_scales(cseed, H, D, spec.sigma, spec.outlier_p, spec.outlier_f)
-                elif spec.calib == "sigma1":
-                    csc = _channel_scales(cseed, H, D, 1.0, spec.outlier_p, spec.outlier_f)
-                else:
-                    raise ValueError(spec.calib)
-                ct = spec.calib_tokens if spec.calib != "rerun" else T
-                calib.append(_gaussian_layer(cseed, csc, ct, H, D, spec.dtype, device))
-        else:
-            n_l = spec.layer_elems
-            if data:
-                parts.append(_edge_layer(spec.kind, seed, n_l, device))
-            if l == 0:
-                calib.append(_edge_layer(spec.kind, cseed, min(n_l, 1 << 20), device))
-    if data:
-        flat = parts[0] if len(parts) == 1 else torch.cat(parts)
-    else:
-        flat = torch.empty(0, dtype=torch.int16 if spec.dtype == BF16 else torch.uint8, device=device)
-    seg = spec.layer_elems if (spec.per_layer_codebooks and L > 1) else 0
+    for l in range(spec.layers):
+        need_calib = spec.per_layer_codebooks or l == 0
+        x, c = _layer(spec, l, device, calib=need_calib)
+        parts.append(x)
+        if need_calib:
+            calib.append(c)
+    flat = parts[0] if len(parts) == 1 else torch.cat(parts)
+    seg = spec.layer_elems if (spec.per_layer_codebooks and spec.layers > 1) else 0
     return Workload(spec=spec, data=flat, calib=calib, segment_elems=seg)
+
+
+def layer(name: str, l: int, device="cpu"):
+    """Layer ``l`` of workload ``name`` on its own: (data, calibration sample)."""
+    return _layer(resize(name), l, device)
 
 
 def random_bits(n: int, dtype: int, seed: int, device="cpu", kind: str = "gaussian",

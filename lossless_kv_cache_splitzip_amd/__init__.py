@@ -1,0 +1,28 @@
+"""libsplitzip: the SplitZip lossless exponent codec for BF16 / FP8 E5M2 KV
+caches on AMD Instinct MI355X (gfx950), hand-written HIP behind a C ABI.
+
+The C ABI is declared in ``include/splitzip.h``; ``_native`` binds it with
+ctypes (marshalling only).  Build the library with
+``python -m lossless_kv_cache_splitzip_amd.build``.
+"""
+from ._native import (  # noqa: F401
+    BF16,
+    E_CAPACITY,
+    E_CODEBOOK,
+    E_CORRUPT,
+    E_HIP,
+    E_INVALID,
+    EXPORTS,
+    FP8_E5M2,
+    LIB_PATH,
+    OK,
+    SplitZipError,
+    compress,
+    decompress,
+    load,
+    splitzip_calibrate,
+    splitzip_compress,
+    splitzip_decompress,
+    splitzip_max_compressed_size,
+    status_string,
+)

@@ -1,0 +1,931 @@
+// libsplitzip -- SplitZip exponent codec for MI355X (gfx950), hand-written HIP.
+//
+// Method: "SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
+// Serving" (arXiv 2605.01708v2).  The pages fix the arithmetic (Spanish
+// technical summary, "Metodologia"): a BF16 value is split into its 8-bit
+// exponent and an 8-bit sign|mantissa byte; the exponent is mapped through an
+// offline top-16 codebook to a 4-bit code, two codes per byte; exponents
+// outside the codebook go to a sparse escape stream of (16-bit position,
+// 8-bit raw exponent); decode maps codes back through a lookup table,
+// recombines, and overwrites the escaped exponents.  The stream layout (SZ1)
+// is stated in include/splitzip.h.
+//
+// GPU design (ours):
+//   prep kernel   header, codebooks, zero padding, clears the scan workspace.
+//   encode        one pass over the input.  A workgroup of 256 threads owns
+//                 an 8192-element tile: coalesced 16-byte loads, a 256-entry
+//                 exponent->code table in LDS, nibble and sign|mantissa
+//                 packing with byte-permute ops, coalesced stores.  Escapes
+//                 are ranked in element order with a wave64 DPP scan and an
+//                 LDS block scan, staged in LDS, and placed by a device-wide
+//                 decoupled look-back over tile aggregates (tile order comes
+//                 from an atomic ticket, so every awaited tile is resident).
+//   decode        a workgroup owns a 16384-element tile inside one chunk.  It
+//                 binary-searches its slice of the chunk's escape records,
+//                 stages them in LDS (bitmap + values), then rebuilds values
+//                 with the 16-entry LUT held in four registers (v_perm_b32
+//                 lookups) and patches escapes in registers before the store.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "splitzip.h"
+
+namespace {
+
+constexpr uint64_t kChunk = 65536;
+constexpr int kThreads = 256;
+constexpr uint64_t kEncTile = 8192;   // elements per encode workgroup
+constexpr uint64_t kDecTile = 16384;  // elements per decode workgroup
+constexpr uint32_t kMagic = 0x00315A53u;
+constexpr uint32_t kMaxK = 65535;
+constexpr uint64_t kMaxN = 1ull << 40;
+constexpr int kCbPerPrep = 128;
+constexpr uint64_t kFlagAgg = 1ull << 62;
+constexpr uint64_t kFlagInc = 1ull << 63;
+constexpr uint64_t kValMask = kFlagAgg - 1;
+constexpr uint8_t kEsc = 0x10;  // table entry of an exponent outside the codebook
+
+__host__ __device__ inline uint64_t round256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+__host__ __device__ inline uint64_t divup(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+struct Sections {
+  uint64_t chunks, offsets, nib, sm, esc, sm_bytes;
+};
+
+__host__ __device__ inline Sections sections_of(int dtype, uint64_t n, uint64_t k) {
+  Sections s;
+  s.chunks = divup(n, kChunk);
+  s.offsets = 64 + 16 * k;
+  s.nib = round256(s.offsets + 8 * (s.chunks + 1));
+  s.sm_bytes = dtype == SPLITZIP_BF16 ? n : 3 * divup(n, 8);
+  s.sm = s.nib + round256(divup(n, 2));
+  s.esc = s.sm + round256(s.sm_bytes);
+  return s;
+}
+
+// Encoder workspace (ticket + one status word per tile) sits after the
+// largest possible stream.
+__host__ __device__ inline uint64_t workspace_offset(int dtype, uint64_t n, uint64_t k) {
+  return round256(sections_of(dtype, n, k).esc + 3 * n);
+}
+
+// ----------------------------------------------------------------- helpers
+__device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Inclusive prefix sum across a wave64: DPP row shifts inside each 16-lane
+// row, then the row totals are carried with readlane.  All 64 lanes active.
+__device__ inline uint32_t wave_inclusive_sum(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15);
+  const uint32_t r1 = __builtin_amdgcn_readlane(v, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 47);
+  const uint32_t row = __lane_id() >> 4;
+  uint32_t carry = 0;
+  carry += row >= 1 ? r0 : 0u;
+  carry += row >= 2 ? r1 : 0u;
+  carry += row >= 3 ? r2 : 0u;
+  return v + carry;
+}
+
+// Decoupled look-back (single thread).  Publishes this tile's aggregate,
+// sums predecessors back to the first inclusive prefix, publishes the
+// inclusive prefix and returns the exclusive one.  A tile only waits on
+// lower tickets, which belong to workgroups already running, and tile 0
+// never waits, so every wait ends.
+__device__ uint64_t look_back(uint64_t* status, uint64_t tile, uint64_t agg) {
+  if (tile == 0) {
+    __hip_atomic_store(&status[0], kFlagInc | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return 0;
+  }
+  __hip_atomic_store(&status[tile], kFlagAgg | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t base = 0;
+  uint64_t j = tile - 1;
+  for (;;) {
+    const uint64_t s = __hip_atomic_load(&status[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((s & (kFlagAgg | kFlagInc)) == 0) {
+      __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    base += s & kValMask;
+    if (s & kFlagInc) break;
+    --j;
+  }
+  __hip_atomic_store(&status[tile], kFlagInc | (base + agg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return base;
+}
+
+// 4 table entries (code | escape flag << 4), one per byte, for BF16 word pair.
+__device__ inline uint32_t gather4(uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3) {
+  return t0 | (t1 << 8) | (t2 << 16) | (t3 << 24);
+}
+
+// Two words of per-byte codes (elements 0..3 and 4..7) -> 8 nibbles, even
+// element low.
+__device__ inline uint32_t pack_nibbles(uint32_t a, uint32_t b) {
+  uint32_t ca = a & 0x0F0F0F0Fu, cb = b & 0x0F0F0F0Fu;
+  ca |= ca >> 4;  // byte0 = c0 | c1 << 4, byte2 = c2 | c3 << 4
+  cb |= cb >> 4;
+  return perm(cb, ca, 0x06040200u);
+}
+
+// Register-array reads with a run-time index, as selects (no scratch memory).
+__device__ inline uint32_t pick4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t i) {
+  return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : a3;
+}
+
+// Element-order bit mask of the escape flags (bit 4 of each byte) of a word
+// of four table entries: flag of byte k -> bit k.
+__device__ inline uint32_t flag_mask4(uint32_t codes) {
+  const uint32_t t = (codes >> 4) & 0x01010101u;
+  return ((t * 0x01020408u) >> 24) & 0xFu;
+}
+
+__device__ inline uint32_t keep_low_bytes(uint32_t nbytes) {
+  return nbytes >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nbytes)) - 1u);
+}
+
+// Codebook lookup of four 4-bit codes (one per byte of s; bits above 3 of
+// each byte are ignored) through the 16-entry LUT held in l0..l3.
+__device__ inline uint32_t lut4(uint32_t s, uint32_t l0, uint32_t l1, uint32_t l2, uint32_t l3) {
+  const uint32_t idx = s & 0x07070707u;
+  const uint32_t lo = perm(l1, l0, idx);
+  const uint32_t hi = perm(l3, l2, idx);
+  // selector 12 yields 0x00, 13 yields 0xFF: a byte mask from code bit 3
+  const uint32_t m = perm(0u, 0u, ((s >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+  return (hi & m) | (lo & ~m);
+}
+
+// Spread 4 nibbles (the 16 bits at bit offset 16*half of w) into 4 bytes
+// (low nibble of each byte valid, high nibble garbage).
+__device__ inline uint32_t spread4(uint32_t w, int half) {
+  const uint32_t t = perm(w, w, half ? 0x03030202u : 0x01010000u);
+  return (t & 0x000F000Fu) | ((t >> 4) & 0x0F000F00u);
+}
+
+// ------------------------------------------------------------- prep kernel
+struct PrepArgs {
+  uint8_t* out;
+  uint64_t n, seg_stored, nib, sm, esc, sm_bytes, offsets, chunks;
+  uint64_t* status;
+  uint64_t n_status;
+  uint32_t* ticket;
+  uint64_t* out_bytes;
+  uint32_t k, dtype, cb_first, cb_count, main;
+  uint8_t cbs[kCbPerPrep * 16];
+};
+
+__device__ inline void put_le(uint8_t* p, uint64_t v, int bytes) {
+  for (int i = 0; i < bytes; ++i) p[i] = (uint8_t)(v >> (8 * i));
+}
+
+__global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
+  const uint64_t gtid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  const uint64_t gsize = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t i = gtid; i < (uint64_t)a.cb_count * 16; i += gsize)
+    a.out[64 + 16 * (uint64_t)a.cb_first + i] = a.cbs[i];
+  if (!a.main) return;
+  for (uint64_t i = gtid; i < a.n_status; i += gsize) a.status[i] = 0;
+  if (blockIdx.x != 0) return;
+  const uint32_t t = threadIdx.x;
+  if (t == 0) *a.ticket = 0;
+  // zero padding after the offsets, the nibbles and the sign|mantissa bytes
+  const uint64_t ends[3] = {a.offsets + 8 * (a.chunks + 1), a.nib + divup(a.n, 2), a.sm + a.sm_bytes};
+  const uint64_t stops[3] = {a.nib, a.sm, a.esc};
+  for (int r = 0; r < 3; ++r)
+    if (ends[r] + t < stops[r]) a.out[ends[r] + t] = 0;
+  if (t < 64) {
+    // header: byte t of the 64-byte header
+    uint8_t b = 0;
+    uint64_t v = 0;
+    int off = 0;
+    if (t < 4) { v = kMagic; off = t; }
+    else if (t < 6) { v = 1; off = t - 4; }
+    else if (t == 6) { v = a.dtype; }
+    else if (t == 7) { v = 16; }
+    else if (t < 16) { v = a.n; off = t - 8; }
+    else if (t < 32) { v = (a.n == 0 && t >= 24) ? a.esc : 0; off = t & 7; }  // E and S (final when n == 0)
+    else if (t < 36) { v = a.chunks; off = t - 32; }
+    else if (t < 40) { v = a.k; off = t - 36; }
+    else if (t < 48) { v = a.seg_stored; off = t - 40; }
+    b = (uint8_t)(v >> (8 * off));
+    a.out[t] = b;
+  }
+  if (a.n == 0 && t == 0) {
+    put_le(a.out + a.offsets, 0, 8);
+    if (a.out_bytes) *a.out_bytes = a.esc;
+  }
+}
+
+// ---------------------------------------------------------- encode kernels
+struct EncArgs {
+  const uint8_t* in;
+  uint8_t* out;
+  uint64_t n, n_tiles, offsets, nib, sm, esc, chunks;
+  uint64_t seg_chunks;  // chunks per codebook segment, 0 when one codebook
+  uint32_t* ticket;
+  uint64_t* status;
+  uint64_t* out_bytes;
+};
+
+// Workgroup epilogue shared by both element types: rank -> global record
+// index through the look-back, record stores, chunk offsets, header totals.
+__device__ inline void emit_escapes(const EncArgs& a, uint64_t tile, uint32_t agg, const uint16_t* st_pos,
+                                    const uint8_t* st_val, uint64_t* s_base) {
+  if (threadIdx.x == 0) {
+    const uint64_t base = look_back(a.status, tile, agg);
+    *s_base = base;
+    if ((tile & 7) == 0) put_le(a.out + a.offsets + 8 * (tile >> 3), base, 8);
+    if (tile == a.n_tiles - 1) {
+      const uint64_t e = std::min<uint64_t>(base + agg, a.n);
+      const uint64_t s = a.esc + 3 * e;
+      put_le(a.out + a.offsets + 8 * a.chunks, e, 8);
+      put_le(a.out + 16, e, 8);
+      put_le(a.out + 24, s, 8);
+      if (a.out_bytes) *a.out_bytes = s;
+    }
+  }
+  __syncthreads();
+  const uint64_t base = *s_base;
+  // a tile holds at most kEncTile escapes and the stream at most n; the
+  // bounds below always hold for a correct scan and keep every store inside
+  // the stream even if they did not
+  const uint32_t lim = (uint32_t)std::min<uint64_t>(std::min<uint64_t>(agg, kEncTile), base < a.n ? a.n - base : 0);
+  for (uint32_t r = threadIdx.x; r < lim; r += kThreads) {
+    uint8_t* d = a.out + a.esc + 3 * (base + r);
+    const uint32_t p = st_pos[r];
+    d[0] = (uint8_t)p;
+    d[1] = (uint8_t)(p >> 8);
+    d[2] = st_val[r];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void encode_bf16_kernel(EncArgs a) {
+  __shared__ uint8_t table[256];
+  __shared__ uint16_t st_pos[kEncTile];
+  __shared__ uint8_t st_val[kEncTile];
+  __shared__ uint32_t s_wave[2][4];
+  __shared__ uint32_t s_tile;
+  __shared__ uint64_t s_base;
+
+  const uint32_t tid = threadIdx.x;
+  if (tid == 0) s_tile = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  table[tid] = kEsc;
+  __syncthreads();
+  const uint64_t tile = s_tile;
+  const uint64_t cbi = a.seg_chunks ? (tile >> 3) / a.seg_chunks : 0;
+  if (tid < 16) table[a.out[64 + 16 * cbi + tid]] = (uint8_t)tid;
+  __syncthreads();
+
+  const uint64_t first = tile * kEncTile;
+  const uint16_t* in16 = reinterpret_cast<const uint16_t*>(a.in);
+  uint4 w[4];
+  uint32_t valid[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint64_t e0 = first + g * 2048 + 8 * tid;
+    valid[g] = e0 >= a.n ? 0u : (uint32_t)std::min<uint64_t>(8, a.n - e0);
+    if (valid[g] == 8) {
+      w[g] = *reinterpret_cast<const uint4*>(in16 + e0);
+    } else {
+      uint32_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
+      for (uint32_t j = 0; j < valid[g]; ++j) {
+        const uint32_t x = (uint32_t)in16[e0 + j] << (16 * (j & 1));
+        if (j < 2) v0 |= x;
+        else if (j < 4) v1 |= x;
+        else if (j < 6) v2 |= x;
+        else v3 |= x;
+      }
+      w[g] = make_uint4(v0, v1, v2, v3);
+    }
+  }
+
+  uint32_t codes_lo[4], codes_hi[4], cnt[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint4 x = w[g];
+    uint32_t lo = gather4(table[(x.x >> 7) & 0xFF], table[(x.x >> 23) & 0xFF], table[(x.y >> 7) & 0xFF],
+                          table[(x.y >> 23) & 0xFF]);
+    uint32_t hi = gather4(table[(x.z >> 7) & 0xFF], table[(x.z >> 23) & 0xFF], table[(x.w >> 7) & 0xFF],
+                          table[(x.w >> 23) & 0xFF]);
+    if (valid[g] < 8) {
+      lo &= keep_low_bytes(valid[g]);
+      hi &= valid[g] > 4 ? keep_low_bytes(valid[g] - 4) : 0u;
+    }
+    codes_lo[g] = lo;
+    codes_hi[g] = hi;
+    cnt[g] = __builtin_popcount(lo & 0x10101010u) + __builtin_popcount(hi & 0x10101010u);
+
+    const uint32_t nib = pack_nibbles(lo, hi);
+    // sign|mantissa: high bytes and low bytes of the four BF16 pairs
+    const uint32_t h01 = perm(x.y, x.x, 0x07050301u), l01 = perm(x.y, x.x, 0x06040200u);
+    const uint32_t h23 = perm(x.w, x.z, 0x07050301u), l23 = perm(x.w, x.z, 0x06040200u);
+    const uint32_t sm0 = (h01 & 0x80808080u) | (l01 & 0x7F7F7F7Fu);
+    const uint32_t sm1 = (h23 & 0x80808080u) | (l23 & 0x7F7F7F7Fu);
+    const uint64_t e0 = first + g * 2048 + 8 * tid;
+    if (valid[g] == 8) {
+      *reinterpret_cast<uint32_t*>(a.out + a.nib + e0 / 2) = nib;
+      *reinterpret_cast<uint2*>(a.out + a.sm + e0) = make_uint2(sm0, sm1);
+    } else if (valid[g] > 0) {
+      for (uint32_t b = 0; b < (valid[g] + 1) / 2; ++b) a.out[a.nib + e0 / 2 + b] = (uint8_t)(nib >> (8 * b));
+      for (uint32_t j = 0; j < valid[g]; ++j)
+        a.out[a.sm + e0 + j] = (uint8_t)((j < 4 ? sm0 : sm1) >> (8 * (j & 3)));
+    }
+  }
+
+  // element-order ranks: groups are ordered (g, thread), so scan the four
+  // per-thread counts as 16-bit fields (a group holds at most 2048 escapes)
+  const uint32_t p01 = cnt[0] | (cnt[1] << 16), p23 = cnt[2] | (cnt[3] << 16);
+  const uint32_t i01 = wave_inclusive_sum(p01), i23 = wave_inclusive_sum(p23);
+  const uint32_t wave = tid >> 6;
+  if ((tid & 63) == 63) {
+    s_wave[0][wave] = i01;
+    s_wave[1][wave] = i23;
+  }
+  __syncthreads();
+  uint32_t pre01 = 0, pre23 = 0, tot01 = 0, tot23 = 0;
+#pragma unroll
+  for (uint32_t v = 0; v < 4; ++v) {
+    const uint32_t x = s_wave[0][v], y = s_wave[1][v];
+    pre01 += v < wave ? x : 0u;
+    pre23 += v < wave ? y : 0u;
+    tot01 += x;
+    tot23 += y;
+  }
+  const uint32_t g0 = tot01 & 0xFFFF, g1 = tot01 >> 16, g2 = tot23 & 0xFFFF, g3 = tot23 >> 16;
+  const uint32_t agg = g0 + g1 + g2 + g3;
+  const uint32_t x01 = pre01 + i01 - p01, x23 = pre23 + i23 - p23;
+  uint32_t rank[4] = {x01 & 0xFFFF, g0 + (x01 >> 16), g0 + g1 + (x23 & 0xFFFF), g0 + g1 + g2 + (x23 >> 16)};
+
+  const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTile;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    if (cnt[g] == 0) continue;
+    uint32_t r = rank[g];
+    uint32_t m = flag_mask4(codes_lo[g]) | (flag_mask4(codes_hi[g]) << 4);
+    const uint64_t e0 = first + g * 2048 + 8 * tid;
+    while (m) {  // escaped elements of this group, in element order
+      const uint32_t j = __builtin_ctz(m);
+      m &= m - 1;
+      if (r < kEncTile) {
+        st_pos[r] = (uint16_t)(in_chunk + g * 2048 + 8 * tid + j);
+        st_val[r] = (uint8_t)(in16[e0 + j] >> 7);
+      }
+      ++r;
+    }
+  }
+  emit_escapes(a, tile, agg, st_pos, st_val, &s_base);
+}
+
+// E5M2: a thread owns 32 consecutive elements (32 input bytes, 16 nibble
+// bytes, 12 sign|mantissa bytes).
+__device__ inline uint32_t signmant12(uint32_t w) {
+  // byte k -> 3-bit value sign<<2 | mantissa, then 4 x 3 bits -> 12 bits
+  const uint32_t u = ((w >> 5) & 0x04040404u) | (w & 0x03030303u);
+  const uint32_t v = u | (u >> 5);          // bits 0..5: e0|e1<<3 ; bits 16..21: e2|e3<<3
+  return (v & 0x3Fu) | ((v >> 10) & 0xFC0u);
+}
+
+__global__ __launch_bounds__(kThreads) void encode_e5m2_kernel(EncArgs a) {
+  __shared__ uint8_t table[32];
+  __shared__ uint16_t st_pos[kEncTile];
+  __shared__ uint8_t st_val[kEncTile];
+  __shared__ uint32_t s_wave[4];
+  __shared__ uint32_t s_tile;
+  __shared__ uint64_t s_base;
+
+  const uint32_t tid = threadIdx.x;
+  if (tid == 0) s_tile = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < 32) table[tid] = kEsc;
+  __syncthreads();
+  const uint64_t tile = s_tile;
+  const uint64_t cbi = a.seg_chunks ? (tile >> 3) / a.seg_chunks : 0;
+  if (tid < 16) table[a.out[64 + 16 * cbi + tid]] = (uint8_t)tid;
+  __syncthreads();
+
+  const uint64_t e0 = tile * kEncTile + 32 * tid;
+  const uint32_t valid = e0 >= a.n ? 0u : (uint32_t)std::min<uint64_t>(32, a.n - e0);
+  uint32_t w[8];
+  if (valid == 32) {
+    const uint4 v0 = *reinterpret_cast<const uint4*>(a.in + e0);
+    const uint4 v1 = *reinterpret_cast<const uint4*>(a.in + e0 + 16);
+    w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+    w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      w[k] = 0;
+      for (uint32_t b = 0; b < 4 && 4 * k + b < valid; ++b) w[k] |= (uint32_t)a.in[e0 + 4 * k + b] << (8 * b);
+    }
+  }
+  uint32_t codes[8];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t x = w[k];
+    uint32_t c = gather4(table[(x >> 2) & 0x1F], table[(x >> 10) & 0x1F], table[(x >> 18) & 0x1F],
+                         table[(x >> 26) & 0x1F]);
+    if (valid < 32) {
+      const uint32_t have = valid > 4u * k ? valid - 4u * k : 0u;
+      c &= keep_low_bytes(have);
+    }
+    codes[k] = c;
+    cnt += __builtin_popcount(c & 0x10101010u);
+  }
+  uint32_t nib[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) nib[d] = pack_nibbles(codes[2 * d], codes[2 * d + 1]);
+  uint32_t g24[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) g24[d] = signmant12(w[2 * d]) | (signmant12(w[2 * d + 1]) << 12);
+  const uint32_t s0 = g24[0] | (g24[1] << 24);
+  const uint32_t s1 = (g24[1] >> 8) | (g24[2] << 16);
+  const uint32_t s2 = (g24[2] >> 16) | (g24[3] << 8);
+  const uint64_t smo = a.sm + 3 * (e0 / 8);
+  if (valid == 32) {
+    *reinterpret_cast<uint4*>(a.out + a.nib + e0 / 2) = make_uint4(nib[0], nib[1], nib[2], nib[3]);
+    uint32_t* sp = reinterpret_cast<uint32_t*>(a.out + smo);
+    sp[0] = s0;
+    sp[1] = s1;
+    sp[2] = s2;
+  } else if (valid > 0) {
+    for (uint32_t b = 0; b < (valid + 1) / 2; ++b)
+      a.out[a.nib + e0 / 2 + b] = (uint8_t)(pick4(nib[0], nib[1], nib[2], nib[3], b >> 2) >> (8 * (b & 3)));
+    for (uint32_t b = 0; b < 3 * ((valid + 7) / 8); ++b)
+      a.out[smo + b] = (uint8_t)(pick4(s0, s1, s2, 0u, b >> 2) >> (8 * (b & 3)));
+  }
+
+  const uint32_t inc = wave_inclusive_sum(cnt);
+  const uint32_t wave = tid >> 6;
+  if ((tid & 63) == 63) s_wave[wave] = inc;
+  __syncthreads();
+  uint32_t pre = 0, agg = 0;
+#pragma unroll
+  for (uint32_t v = 0; v < 4; ++v) {
+    pre += v < wave ? s_wave[v] : 0u;
+    agg += s_wave[v];
+  }
+  if (cnt) {
+    uint32_t r = pre + inc - cnt;
+    const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTile + 32 * tid;
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m |= flag_mask4(codes[k]) << (4 * k);
+    while (m) {  // escaped elements, in element order
+      const uint32_t j = __builtin_ctz(m);
+      m &= m - 1;
+      if (r < kEncTile) {
+        st_pos[r] = (uint16_t)(in_chunk + j);
+        st_val[r] = (uint8_t)((a.in[e0 + j] >> 2) & 0x1F);
+      }
+      ++r;
+    }
+  }
+  emit_escapes(a, tile, agg, st_pos, st_val, &s_base);
+}
+
+// ---------------------------------------------------------- decode kernels
+struct DecArgs {
+  const uint8_t* in;
+  uint64_t in_bytes;
+  uint8_t* out;
+  uint64_t n;
+  int32_t* status;
+  int dtype;
+};
+
+struct Header {
+  uint64_t k, seg, e, chunks;
+  Sections s;
+};
+
+__device__ inline uint64_t ld64(const uint8_t* p) { return *reinterpret_cast<const uint64_t*>(p); }
+__device__ inline uint32_t ld32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+// Header checks shared by every workgroup (all reads inside the first 64
+// bytes; in_bytes >= 64 is checked on the host).
+__device__ bool read_header(const DecArgs& a, Header& h) {
+  const uint8_t* in = a.in;
+  const uint32_t w0 = ld32(in), w1 = ld32(in + 4);
+  if (w0 != kMagic) return false;
+  if ((w1 & 0xFFFF) != 1 || ((w1 >> 16) & 0xFF) != (uint32_t)a.dtype || (w1 >> 24) != 16) return false;
+  if (ld64(in + 8) != a.n) return false;
+  if (ld64(in + 48) != 0 || ld64(in + 56) != 0) return false;
+  h.e = ld64(in + 16);
+  const uint64_t total = ld64(in + 24);
+  h.chunks = ld32(in + 32);
+  h.k = ld32(in + 36);
+  h.seg = ld64(in + 40);
+  if (h.chunks != divup(a.n, kChunk)) return false;
+  if (h.k == 0 || h.k > kMaxK) return false;
+  if (h.k == 1) {
+    if (h.seg != a.n) return false;
+  } else if (h.seg == 0 || (h.seg % kChunk) != 0 || h.seg < divup(a.n, h.k)) {
+    return false;
+  }
+  if (h.e > a.n) return false;
+  h.s = sections_of(a.dtype, a.n, h.k);
+  if (total != h.s.esc + 3 * h.e || total > a.in_bytes) return false;
+  return true;
+}
+
+__device__ inline void report_corrupt(int32_t* status) {
+  if (status) __hip_atomic_store(status, (int32_t)SPLITZIP_E_CORRUPT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint32_t record_pos(const uint8_t* rec) { return rec[0] | ((uint32_t)rec[1] << 8); }
+
+// First record index in [lo, hi) whose position is >= key (positions are
+// ascending in a valid stream; a corrupt order is caught by the caller).
+__device__ uint64_t lower_bound_pos(const uint8_t* esc, uint64_t lo, uint64_t hi, uint32_t key) {
+  while (lo < hi) {
+    const uint64_t mid = lo + (hi - lo) / 2;
+    if (record_pos(esc + 3 * mid) < key) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Stage this tile's escapes in LDS: a bitmap over the tile's elements and
+// the raw exponents.  Returns false (uniformly) if the stream is invalid.
+__device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, uint32_t* bitmap, uint8_t* vals,
+                              uint32_t* s_range, int* s_err) {
+  const uint32_t tid = threadIdx.x;
+  const uint64_t chunk = tile / (kChunk / kDecTile);
+  const uint32_t q = (uint32_t)(tile % (kChunk / kDecTile));
+  const uint64_t chunk_len = std::min<uint64_t>(kChunk, a.n - chunk * kChunk);
+  const uint32_t win_lo = q * (uint32_t)kDecTile;
+  const uint32_t win_len = (uint32_t)std::min<uint64_t>(kDecTile, chunk_len - win_lo);
+  const bool last_in_chunk = win_lo + win_len == chunk_len;
+  const uint8_t* offs = a.in + h.s.offsets;
+  const uint64_t lo = ld64(offs + 8 * chunk), hi = ld64(offs + 8 * (chunk + 1));
+  bool ok = lo <= hi && hi <= h.e;
+  if (chunk == 0 && lo != 0) ok = false;
+  if (chunk == h.chunks - 1 && hi != h.e) ok = false;
+  if (!ok) return false;  // uniform: every thread read the same words
+
+  for (uint32_t i = tid; i < kDecTile / 32; i += kThreads) bitmap[i] = 0;
+  if (tid == 0) {
+    s_range[0] = (uint32_t)((q == 0 ? lo : lower_bound_pos(a.in + h.s.esc, lo, hi, win_lo)) - lo);
+    *s_err = 0;
+  }
+  if (tid == 64) s_range[1] = (uint32_t)((last_in_chunk ? hi : lower_bound_pos(a.in + h.s.esc, lo, hi, win_lo + win_len)) - lo);
+  __syncthreads();
+  const uint64_t ra = lo + s_range[0], rb = lo + s_range[1];
+  const uint32_t vmax = a.dtype == SPLITZIP_BF16 ? 256u : 32u;
+  bool bad = false;
+  for (uint64_t r = ra + tid; r < rb; r += kThreads) {
+    const uint8_t* rec = a.in + h.s.esc + 3 * r;
+    const uint32_t pos = record_pos(rec);
+    const uint32_t v = rec[2];
+    const uint32_t local = pos - win_lo;  // wraps for pos < win_lo
+    bool good = pos >= win_lo && local < win_len && v < vmax;
+    if (good && r > ra) good = record_pos(rec - 3) < pos;
+    if (!good) {
+      bad = true;
+      continue;
+    }
+    vals[local] = (uint8_t)v;
+    atomicOr(&bitmap[local >> 5], 1u << (local & 31));
+  }
+  if (bad) *s_err = 1;
+  __syncthreads();
+  return *s_err == 0;
+}
+
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
+  __shared__ uint32_t bitmap[kDecTile / 32];
+  __shared__ uint8_t vals[kDecTile];
+  __shared__ uint32_t s_range[2];
+  __shared__ int s_err;
+  Header h;
+  if (!read_header(a, h)) {
+    if (threadIdx.x == 0) report_corrupt(a.status);
+    return;
+  }
+  if (a.n == 0) {  // header-only stream: off[0] must be 0
+    if (threadIdx.x == 0 && ld64(a.in + h.s.offsets) != 0) report_corrupt(a.status);
+    return;
+  }
+  const uint64_t tile = blockIdx.x;
+  const uint64_t chunk = tile / (kChunk / kDecTile);
+  const uint64_t cbi = h.k == 1 ? 0 : (chunk * kChunk) / h.seg;
+  const uint8_t* cb = a.in + 64 + 16 * cbi;
+  const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4), l2 = ld32(cb + 8), l3 = ld32(cb + 12);
+  if (!stage_escapes(a, h, tile, bitmap, vals, s_range, &s_err)) {
+    if (threadIdx.x == 0) report_corrupt(a.status);
+    return;
+  }
+  const uint32_t tid = threadIdx.x;
+  const uint64_t first = tile * kDecTile;
+  const uint8_t* bm8 = reinterpret_cast<const uint8_t*>(bitmap);
+  uint16_t* out16 = reinterpret_cast<uint16_t*>(a.out);
+#pragma unroll 2
+  for (int g = 0; g < 8; ++g) {
+    const uint32_t local = g * 2048 + 8 * tid;
+    const uint64_t e0 = first + local;
+    if (e0 >= a.n) break;
+    const uint32_t valid = (uint32_t)std::min<uint64_t>(8, a.n - e0);
+    uint32_t nib;
+    uint2 sm;
+    if (valid == 8) {
+      nib = ld32(a.in + h.s.nib + e0 / 2);
+      sm = *reinterpret_cast<const uint2*>(a.in + h.s.sm + e0);
+    } else {
+      uint32_t tn = 0, t0 = 0, t1 = 0;
+      for (uint32_t b = 0; b < (valid + 1) / 2; ++b) tn |= (uint32_t)a.in[h.s.nib + e0 / 2 + b] << (8 * b);
+      for (uint32_t j = 0; j < valid; ++j) {
+        const uint32_t x = (uint32_t)a.in[h.s.sm + e0 + j] << (8 * (j & 3));
+        if (j < 4) t0 |= x;
+        else t1 |= x;
+      }
+      nib = tn;
+      sm = make_uint2(t0, t1);
+    }
+    uint32_t e_lo = lut4(spread4(nib, 0), l0, l1, l2, l3);
+    uint32_t e_hi = lut4(spread4(nib, 1), l0, l1, l2, l3);
+    uint32_t mask = bm8[local >> 3];
+    while (mask) {  // escape overwrite, before the values are assembled
+      const uint32_t j = __builtin_ctz(mask);
+      mask &= mask - 1;
+      const uint32_t v = vals[local + j];
+      const uint32_t sh = 8 * (j & 3);
+      if (j < 4) e_lo = (e_lo & ~(0xFFu << sh)) | (v << sh);
+      else e_hi = (e_hi & ~(0xFFu << sh)) | (v << sh);
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint32_t e = half ? e_hi : e_lo;
+      const uint32_t m = half ? sm.y : sm.x;
+      const uint32_t hi = (m & 0x80808080u) | ((e >> 1) & 0x7F7F7F7Fu);
+      const uint32_t lo = ((e << 7) & 0x80808080u) | (m & 0x7F7F7F7Fu);
+      o[2 * half] = perm(hi, lo, 0x05010400u);
+      o[2 * half + 1] = perm(hi, lo, 0x07030602u);
+    }
+    if (valid == 8) {
+      *reinterpret_cast<uint4*>(out16 + e0) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+      for (uint32_t j = 0; j < valid; ++j)
+        out16[e0 + j] = (uint16_t)(pick4(o[0], o[1], o[2], o[3], j >> 1) >> (16 * (j & 1)));
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
+  __shared__ uint32_t bitmap[kDecTile / 32];
+  __shared__ uint8_t vals[kDecTile];
+  __shared__ uint32_t s_range[2];
+  __shared__ int s_err;
+  Header h;
+  if (!read_header(a, h)) {
+    if (threadIdx.x == 0) report_corrupt(a.status);
+    return;
+  }
+  if (a.n == 0) {  // header-only stream: off[0] must be 0
+    if (threadIdx.x == 0 && ld64(a.in + h.s.offsets) != 0) report_corrupt(a.status);
+    return;
+  }
+  const uint64_t tile = blockIdx.x;
+  const uint64_t chunk = tile / (kChunk / kDecTile);
+  const uint64_t cbi = h.k == 1 ? 0 : (chunk * kChunk) / h.seg;
+  const uint8_t* cb = a.in + 64 + 16 * cbi;
+  const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4), l2 = ld32(cb + 8), l3 = ld32(cb + 12);
+  if (((l0 | l1 | l2 | l3) & 0xE0E0E0E0u) != 0) {  // E5M2 exponents are 5 bits
+    if (threadIdx.x == 0) report_corrupt(a.status);
+    return;
+  }
+  if (!stage_escapes(a, h, tile, bitmap, vals, s_range, &s_err)) {
+    if (threadIdx.x == 0) report_corrupt(a.status);
+    return;
+  }
+  const uint32_t tid = threadIdx.x;
+  const uint64_t first = tile * kDecTile;
+#pragma unroll 1
+  for (int g = 0; g < 2; ++g) {
+    const uint32_t local = g * 8192 + 32 * tid;
+    const uint64_t e0 = first + local;
+    if (e0 >= a.n) break;
+    const uint32_t valid = (uint32_t)std::min<uint64_t>(32, a.n - e0);
+    uint32_t nib[4], sw[3];
+    const uint64_t smo = h.s.sm + 3 * (e0 / 8);
+    if (valid == 32) {
+      const uint4 v = *reinterpret_cast<const uint4*>(a.in + h.s.nib + e0 / 2);
+      nib[0] = v.x; nib[1] = v.y; nib[2] = v.z; nib[3] = v.w;
+      sw[0] = ld32(a.in + smo);
+      sw[1] = ld32(a.in + smo + 4);
+      sw[2] = ld32(a.in + smo + 8);
+    } else {
+      const uint32_t nb = (valid + 1) / 2, sb = 3 * ((valid + 7) / 8);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        nib[k] = 0;
+        for (uint32_t b = 0; b < 4 && 4 * k + b < nb; ++b) nib[k] |= (uint32_t)a.in[h.s.nib + e0 / 2 + 4 * k + b] << (8 * b);
+      }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        sw[k] = 0;
+        for (uint32_t b = 0; b < 4 && 4 * k + b < sb; ++b) sw[k] |= (uint32_t)a.in[smo + 4 * k + b] << (8 * b);
+      }
+    }
+    const uint32_t esc_bits = bitmap[local >> 5];
+    uint32_t o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t e = lut4(spread4(nib[k >> 1], k & 1), l0, l1, l2, l3);
+      uint32_t mk = (esc_bits >> (4 * k)) & 0xFu;
+      while (mk) {  // escape overwrite of elements 4k..4k+3
+        const uint32_t j = __builtin_ctz(mk);
+        mk &= mk - 1;
+        const uint32_t sh = 8 * j;
+        e = (e & ~(0xFFu << sh)) | ((uint32_t)vals[local + 4 * k + j] << sh);
+      }
+      // 12 bits of sign|mantissa triples for elements 4k..4k+3
+      const int bit = 12 * k;
+      const int word = bit >> 5, sh = bit & 31;
+      const uint32_t hiw = word + 1 < 3 ? sw[word + 1] : 0u;
+      const uint32_t v12 = (uint32_t)(((((uint64_t)hiw) << 32) | sw[word]) >> sh) & 0xFFFu;
+      const uint32_t y = (v12 & 0x3Fu) | ((v12 & 0xFC0u) << 10);
+      const uint32_t z = (y & 0x00070007u) | ((y << 5) & 0x07000700u);
+      o[k] = ((z & 0x04040404u) << 5) | (e << 2) | (z & 0x03030303u);
+    }
+    if (valid == 32) {
+      *reinterpret_cast<uint4*>(a.out + e0) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(a.out + e0 + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        for (uint32_t b = 0; b < 4 && 4 * k + b < valid; ++b) a.out[e0 + 4 * k + b] = (uint8_t)(o[k] >> (8 * b));
+    }
+  }
+}
+
+__global__ void set_status_kernel(int32_t* status) { *status = SPLITZIP_OK; }
+
+// ------------------------------------------------------------ host helpers
+bool dtype_valid(int dtype) { return dtype == SPLITZIP_BF16 || dtype == SPLITZIP_FP8_E5M2; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+uint32_t exponent_of(int dtype, const void* data, size_t i) {
+  if (dtype == SPLITZIP_BF16) return (static_cast<const uint16_t*>(data)[i] >> 7) & 0xFFu;
+  return (static_cast<const uint8_t*>(data)[i] >> 2) & 0x1Fu;
+}
+
+int codebooks_valid(int dtype, const uint8_t* cbs, uint32_t k) {
+  const uint32_t limit = dtype == SPLITZIP_BF16 ? 256u : 32u;
+  for (uint32_t c = 0; c < k; ++c) {
+    uint32_t seen[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t v = cbs[16 * c + i];
+      if (v >= limit || (seen[v >> 5] >> (v & 31)) & 1u) return 0;
+      seen[v >> 5] |= 1u << (v & 31);
+    }
+  }
+  return 1;
+}
+
+}  // namespace
+
+// ================================================================== C ABI
+extern "C" {
+
+int splitzip_calibrate(int dtype, const void* host_samples, size_t n_elems, uint8_t codebook_out[16]) {
+  if (!dtype_valid(dtype) || codebook_out == nullptr || (host_samples == nullptr && n_elems > 0))
+    return SPLITZIP_E_INVALID;
+  const uint32_t values = dtype == SPLITZIP_BF16 ? 256u : 32u;
+  uint64_t count[256] = {};
+  for (size_t i = 0; i < n_elems; ++i) ++count[exponent_of(dtype, host_samples, i)];
+  uint32_t order[256];
+  for (uint32_t v = 0; v < values; ++v) order[v] = v;
+  std::stable_sort(order, order + values, [&](uint32_t x, uint32_t y) { return count[x] > count[y]; });
+  for (int k = 0; k < 16; ++k) codebook_out[k] = static_cast<uint8_t>(order[k]);
+  return SPLITZIP_OK;
+}
+
+size_t splitzip_max_compressed_size(int dtype, size_t n_elems, uint32_t n_codebooks) {
+  if (!dtype_valid(dtype) || n_codebooks == 0 || n_codebooks > kMaxK || n_elems > kMaxN) return 0;
+  return workspace_offset(dtype, n_elems, n_codebooks) + 256 + 8 * divup(n_elems, kEncTile);
+}
+
+int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks, uint32_t n_codebooks,
+                      size_t segment_elems, void* d_out, size_t out_capacity, uint64_t* d_out_bytes,
+                      hipStream_t stream) {
+  if (!dtype_valid(dtype) || n_elems > kMaxN || h_codebooks == nullptr || n_codebooks == 0 || n_codebooks > kMaxK)
+    return SPLITZIP_E_INVALID;
+  if ((d_in == nullptr && n_elems > 0) || d_out == nullptr || !aligned(d_in, 16) || !aligned(d_out, 16) ||
+      !aligned(d_out_bytes, 8))
+    return SPLITZIP_E_INVALID;
+  if (n_codebooks > 1 && (segment_elems == 0 || segment_elems % kChunk != 0 || segment_elems < divup(n_elems, n_codebooks)))
+    return SPLITZIP_E_INVALID;
+  if (!codebooks_valid(dtype, h_codebooks, n_codebooks)) return SPLITZIP_E_CODEBOOK;
+  if (out_capacity < splitzip_max_compressed_size(dtype, n_elems, n_codebooks)) return SPLITZIP_E_CAPACITY;
+
+  const uint64_t n = n_elems;
+  const Sections s = sections_of(dtype, n, n_codebooks);
+  const uint64_t n_tiles = divup(n, kEncTile);
+  uint8_t* out = static_cast<uint8_t*>(d_out);
+  const uint64_t ws = workspace_offset(dtype, n, n_codebooks);
+  uint32_t* ticket = reinterpret_cast<uint32_t*>(out + ws);
+  uint64_t* status = reinterpret_cast<uint64_t*>(out + ws + 256);
+
+  for (uint32_t first = 0; first < n_codebooks; first += kCbPerPrep) {
+    PrepArgs p;
+    memset(&p, 0, sizeof(p));
+    p.out = out;
+    p.n = n;
+    p.seg_stored = n_codebooks == 1 ? n : segment_elems;
+    p.nib = s.nib;
+    p.sm = s.sm;
+    p.esc = s.esc;
+    p.sm_bytes = s.sm_bytes;
+    p.offsets = s.offsets;
+    p.chunks = s.chunks;
+    p.status = status;
+    p.n_status = n_tiles;
+    p.ticket = ticket;
+    p.out_bytes = d_out_bytes;
+    p.k = n_codebooks;
+    p.dtype = (uint32_t)dtype;
+    p.cb_first = first;
+    p.cb_count = std::min<uint32_t>(kCbPerPrep, n_codebooks - first);
+    p.main = first == 0;
+    memcpy(p.cbs, h_codebooks + 16ull * first, 16ull * p.cb_count);
+    const uint64_t work = std::max<uint64_t>(p.main ? n_tiles : 0, 16ull * p.cb_count);
+    const uint32_t blocks = (uint32_t)std::min<uint64_t>(1024, std::max<uint64_t>(1, divup(work, kThreads)));
+    prep_kernel<<<blocks, kThreads, 0, stream>>>(p);
+    if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
+  }
+  if (n == 0) return SPLITZIP_OK;
+
+  EncArgs e;
+  e.in = static_cast<const uint8_t*>(d_in);
+  e.out = out;
+  e.n = n;
+  e.n_tiles = n_tiles;
+  e.offsets = s.offsets;
+  e.nib = s.nib;
+  e.sm = s.sm;
+  e.esc = s.esc;
+  e.chunks = s.chunks;
+  e.seg_chunks = n_codebooks == 1 ? 0 : segment_elems / kChunk;
+  e.ticket = ticket;
+  e.status = status;
+  e.out_bytes = d_out_bytes;
+  if (dtype == SPLITZIP_BF16)
+    encode_bf16_kernel<<<(uint32_t)n_tiles, kThreads, 0, stream>>>(e);
+  else
+    encode_e5m2_kernel<<<(uint32_t)n_tiles, kThreads, 0, stream>>>(e);
+  if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
+  return SPLITZIP_OK;
+}
+
+int splitzip_decompress(const void* d_in, size_t in_bytes, int dtype, size_t n_elems, void* d_out, int32_t* d_status,
+                        hipStream_t stream) {
+  if (!dtype_valid(dtype) || n_elems > kMaxN || d_in == nullptr || in_bytes < 64 || !aligned(d_in, 16) ||
+      (d_out == nullptr && n_elems > 0) || !aligned(d_out, 16) || !aligned(d_status, 4))
+    return SPLITZIP_E_INVALID;
+  if (d_status) {
+    set_status_kernel<<<1, 1, 0, stream>>>(d_status);
+    if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
+  }
+  DecArgs a;
+  a.in = static_cast<const uint8_t*>(d_in);
+  a.in_bytes = in_bytes;
+  a.out = static_cast<uint8_t*>(d_out);
+  a.n = n_elems;
+  a.status = d_status;
+  a.dtype = dtype;
+  // one workgroup per 16384-element tile; a header-only stream (n == 0)
+  // still gets one workgroup, which only validates
+  const uint32_t blocks = (uint32_t)std::max<uint64_t>(1, divup(n_elems, kDecTile));
+  if (dtype == SPLITZIP_BF16) {
+    decode_bf16_kernel<<<blocks, kThreads, 0, stream>>>(a);
+  } else {
+    decode_e5m2_kernel<<<blocks, kThreads, 0, stream>>>(a);
+  }
+  if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
+  return SPLITZIP_OK;
+}
+
+const char* splitzip_status_string(int status) {
+  switch (status) {
+    case SPLITZIP_OK: return "ok";
+    case SPLITZIP_E_INVALID: return "invalid argument";
+    case SPLITZIP_E_CAPACITY: return "output capacity too small";
+    case SPLITZIP_E_CODEBOOK: return "invalid codebook";
+    case SPLITZIP_E_CORRUPT: return "corrupt stream";
+    case SPLITZIP_E_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

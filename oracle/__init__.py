@@ -79,6 +79,8 @@ def _bind(lib):
     lib.szo_decompress.restype = i32
     lib.szo_count_escapes.argtypes = [i32, vp, u64, vp, u32, u64]
     lib.szo_count_escapes.restype = u64
+    lib.szo_sections.argtypes = [i32, u64, u32, vp]
+    lib.szo_sections.restype = i32
     return lib
 
 
@@ -107,6 +109,16 @@ def _as_codebooks(codebooks) -> np.ndarray:
 
 def stream_size(dtype: int, n: int, n_codebooks: int, n_escapes: int) -> int:
     return int(_load().szo_stream_size(dtype, n, n_codebooks, n_escapes))
+
+
+def sections(dtype: int, n: int, n_codebooks: int) -> dict:
+    """Section offsets of a stream (chunks, offsets table, nibbles, sign|mantissa, escapes)."""
+    out = np.zeros(5, dtype=np.uint64)
+    rc = _load().szo_sections(dtype, n, n_codebooks, _ptr(out))
+    if rc != OK:
+        raise ValueError(f"szo_sections failed: {rc}")
+    c, off, nib, sm, esc = (int(v) for v in out)
+    return {"chunks": c, "offsets": off, "nib": nib, "sm": sm, "esc": esc}
 
 
 def max_size(dtype: int, n: int, n_codebooks: int) -> int:

@@ -176,6 +176,19 @@ uint64_t szo_stream_size(int dtype, uint64_t n, uint32_t K, uint64_t E) {
   return L.P + 3ull * E;
 }
 
+/* Section offsets of a stream: out[0] = C, out[1] = offset table, out[2] =
+ * nibbles N0, out[3] = sign|mantissa N1, out[4] = escape records P. */
+int szo_sections(int dtype, uint64_t n, uint32_t K, uint64_t out[5]) {
+  if (!dtype_ok(dtype) || out == NULL) return SZO_E_INVALID;
+  szo_layout L = layout_of(dtype, n, K);
+  out[0] = L.C;
+  out[1] = 64 + 16ull * K;
+  out[2] = L.N0;
+  out[3] = L.N1;
+  out[4] = L.P;
+  return SZO_OK;
+}
+
 /* Worst case (every element escapes). */
 uint64_t szo_max_size(int dtype, uint64_t n, uint32_t K) { return szo_stream_size(dtype, n, K, n); }
 

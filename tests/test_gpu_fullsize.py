@@ -1,0 +1,55 @@
+"""Full-size workloads, in the launch configuration the benchmark times: the
+GPU stream equals the oracle's byte for byte (checked section by section
+against per-segment oracle streams), the round trip is bit-exact, and each
+workload has the escape statistics its recipe states."""
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+import oracle as O
+from paritylib import compare_with_oracle
+
+pytestmark = pytest.mark.gpu
+
+sz = pytest.importorskip("lossless_kv_cache_splitzip_amd")
+
+# name -> (min escape rate, max escape rate)
+EXPECT = {
+    "kv_layer_bf16": (0.0005, 0.01),
+    "llama3_8b_kv_bf16": (0.0005, 0.01),          # top-16 coverage >= 99%
+    "long_ctx_heavy_tail_bf16": (0.01, 0.03),     # 1-3% escapes
+    "edge_const_exponent": (0.0, 0.0),            # no escapes
+    "edge_uniform_bits": (15 / 16 - 0.005, 15 / 16 + 0.005),
+    "edge_special_values": (0.0, 0.5),
+    "llama3_70b_kv_e5m2": (0.0005, 0.01),
+}
+
+
+@pytest.mark.parametrize("name", list(EXPECT))
+def test_full_size_workload(name):
+    print(f"case full-size {name}", flush=True)
+    wl = kvsynth.make(name, device="cuda")
+    dtype = wl.spec.dtype
+    cbs = np.stack([sz.splitzip_calibrate(dtype, kvsynth.to_numpy_bits(c)) for c in wl.calib])
+    seg = wl.segment_elems if cbs.shape[0] > 1 else 0
+    out, nb = sz.compress(wl.data, cbs, seg)
+    torch.cuda.synchronize()
+    n_bytes = int(nb.item())
+    y, st = sz.decompress(out[:n_bytes], wl.n, dtype)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(y.view(torch.uint8), wl.data.view(torch.uint8))
+    del y
+    gpu = out[:n_bytes].cpu().numpy()
+    del out
+    xh = kvsynth.to_numpy_bits(wl.data)
+    E = compare_with_oracle(gpu, dtype, xh, cbs, seg)
+    eps = E / wl.n
+    lo, hi = EXPECT[name]
+    print(f"  n={wl.n} K={cbs.shape[0]} escapes={E} rate={eps:.5f} ratio={wl.raw_bytes / n_bytes:.4f}", flush=True)
+    assert lo <= eps <= hi
+    if name == "edge_const_exponent":
+        assert 16 / 12 * 0.999 < wl.raw_bytes / n_bytes < 16 / 12
+    if dtype == O.E5M2:
+        assert wl.raw_bytes / n_bytes < 8 / 7

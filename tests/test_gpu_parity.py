@@ -1,0 +1,246 @@
+"""GPU parity: libsplitzip's streams are byte-identical to the CPU oracle's and
+every round trip is bit-exact (integer work: tolerance 0).
+
+All calls go through the C ABI (ctypes binding in lossless_kv_cache_splitzip_amd).
+"""
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+import oracle as O
+from paritylib import compare_with_oracle, u64
+
+pytestmark = pytest.mark.gpu
+
+sz = pytest.importorskip("lossless_kv_cache_splitzip_amd")
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _bits_np(t):
+    return kvsynth.to_numpy_bits(t)
+
+
+def _gpu_compress(x_dev, cbs, seg):
+    out, nb = sz.compress(x_dev, cbs, seg)
+    torch.cuda.synchronize()
+    n_bytes = int(nb.item())
+    return out, n_bytes
+
+
+def _gpu_roundtrip_ok(out, n_bytes, x_dev, dtype):
+    y, st = sz.decompress(out[:n_bytes], x_dev.numel(), dtype)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    return torch.equal(y.view(torch.uint8), x_dev.view(torch.uint8))
+
+
+def _calibrate(dtype, wl):
+    return np.stack([sz.splitzip_calibrate(dtype, _bits_np(c)) for c in wl.calib])
+
+
+SMALL = [
+    ("kv_layer_bf16", dict(tokens=192)),
+    ("llama3_8b_kv_bf16", dict(layers=3, tokens=64)),
+    ("long_ctx_heavy_tail_bf16", dict(layers=3, tokens=128)),
+    ("edge_const_exponent", dict(tokens=96)),
+    ("edge_uniform_bits", dict(tokens=96)),
+    ("edge_special_values", dict(tokens=96)),
+    ("llama3_70b_kv_e5m2", dict(layers=3, tokens=64)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("ragged", [0, 37])
+def test_small_workloads_byte_identical(name, kw, ragged):
+    """Shrunk workloads (several tiles and chunks, with and without a ragged
+    tail): GPU stream == oracle stream, GPU round trip exact, and each side
+    decodes the other's stream."""
+    wl = kvsynth.make(name, device=DEV, **kw)
+    dtype = wl.spec.dtype
+    x = wl.data[: wl.n - ragged].contiguous()
+    cbs = _calibrate(dtype, wl)
+    seg = wl.segment_elems if cbs.shape[0] > 1 else 0
+    _say(f"case {name} n={x.numel()} K={cbs.shape[0]} seg={seg}")
+    out, nb = _gpu_compress(x, cbs, seg)
+    gpu = out[:nb].cpu().numpy()
+    xh = _bits_np(x)
+    want = O.compress(dtype, xh, cbs, seg)
+    assert gpu.size == want.size
+    assert np.array_equal(gpu, want)
+    assert _gpu_roundtrip_ok(out, nb, x, dtype)
+    # oracle decodes the GPU stream; GPU decodes the oracle stream
+    assert np.array_equal(O.decompress(gpu, dtype, xh.size), xh)
+    ws = torch.from_numpy(want).to(DEV)
+    y, st = sz.decompress(ws, xh.size, dtype)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(_bits_np(y), xh)
+
+
+SIZES = [0, 1, 2, 3, 7, 8, 9, 31, 32, 33, 255, 4097, 8191, 8192, 8193, 16383, 16384, 16385, 40000,
+         65535, 65536, 65537, 131071, 131073, 200003]
+
+
+@pytest.mark.parametrize("dtype", [O.BF16, O.E5M2], ids=["bf16", "e5m2"])
+@pytest.mark.parametrize("kind", ["gaussian", "uniform_bits"])
+def test_edge_sizes(dtype, kind):
+    """Empty, tiny, odd, partial-group, partial-tile and partial-chunk sizes."""
+    for n in SIZES:
+        _say(f"case dtype={dtype} kind={kind} n={n}")
+        xt = kvsynth.random_bits(n, dtype, seed=1000 + n, kind=kind)
+        xh = _bits_np(xt)
+        cb = O.calibrate(dtype, xh[: max(1, n // 3)])
+        x = xt.to(DEV)
+        out, nb = _gpu_compress(x, cb, 0)
+        gpu = out[:nb].cpu().numpy()
+        assert np.array_equal(gpu, O.compress(dtype, xh, cb)), f"n={n}"
+        if n:
+            assert _gpu_roundtrip_ok(out, nb, x, dtype), f"n={n}"
+        else:
+            y, st = sz.decompress(out[:nb], 0, dtype)
+            torch.cuda.synchronize()
+            assert int(st.item()) == 0
+
+
+@pytest.mark.parametrize("dtype", [O.BF16, O.E5M2], ids=["bf16", "e5m2"])
+def test_all_bit_patterns(dtype):
+    """Every BF16 (65,536) / E5M2 (256) pattern -- +-0, subnormals, +-Inf,
+    NaN payloads -- under a codebook that excludes the extreme exponents and
+    one that includes them."""
+    if dtype == O.BF16:
+        allp = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        cbs = [np.arange(120, 136, dtype=np.uint8), np.array([0, 255] + list(range(120, 134)), np.uint8)]
+    else:
+        allp = np.arange(256, dtype=np.uint8)
+        cbs = [np.arange(8, 24, dtype=np.uint8), np.array([0, 31] + list(range(8, 22)), np.uint8)]
+    rng = np.random.default_rng(1)
+    xh = np.concatenate([rng.permutation(allp) for _ in range(3 if dtype == O.BF16 else 700)])
+    x = torch.from_numpy(xh.view(np.int16) if dtype == O.BF16 else xh).to(DEV)
+    for cb in cbs:
+        out, nb = _gpu_compress(x, cb, 0)
+        assert np.array_equal(out[:nb].cpu().numpy(), O.compress(dtype, xh, cb))
+        assert _gpu_roundtrip_ok(out, nb, x, dtype)
+
+
+@pytest.mark.parametrize("dtype", [O.BF16, O.E5M2], ids=["bf16", "e5m2"])
+def test_segment_codebooks(dtype):
+    """K codebooks over segments of whole chunks; the last segment ragged."""
+    K, seg = 4, 2 * 65536
+    n = K * seg - 12345
+    xt = kvsynth.random_bits(n, dtype, seed=77, sigma=1.6)
+    xh = _bits_np(xt)
+    cbs = np.stack([O.calibrate(dtype, xh[k * seg:k * seg + 3000]) for k in range(K)])
+    cbs[2] = cbs[2][::-1].copy()
+    x = xt.to(DEV)
+    out, nb = _gpu_compress(x, cbs, seg)
+    assert np.array_equal(out[:nb].cpu().numpy(), O.compress(dtype, xh, cbs, seg))
+    assert _gpu_roundtrip_ok(out, nb, x, dtype)
+
+
+def test_many_codebooks_multiple_prep_launches():
+    """More codebooks than one prep launch carries (130 > 128)."""
+    K, seg = 130, 65536
+    n = K * seg - 999
+    xt = kvsynth.random_bits(n, O.BF16, seed=5)
+    xh = _bits_np(xt)
+    rng = np.random.default_rng(2)
+    cbs = np.stack([rng.permutation(np.arange(110, 140))[:16].astype(np.uint8) for _ in range(K)])
+    x = xt.to(DEV)
+    out, nb = _gpu_compress(x, cbs, seg)
+    assert np.array_equal(out[:nb].cpu().numpy(), O.compress(O.BF16, xh, cbs, seg))
+    assert _gpu_roundtrip_ok(out, nb, x, O.BF16)
+
+
+@pytest.mark.parametrize("dtype", [O.BF16, O.E5M2], ids=["bf16", "e5m2"])
+def test_deterministic_across_runs_and_streams(dtype):
+    """Race check: the escape compaction is order-dependent, so any race shows
+    up as a byte difference.  Five encodes on different streams, one with
+    another kernel running beside it, must give the same bytes."""
+    n = 3 * 1048576 + 11
+    xt = kvsynth.random_bits(n, dtype, seed=31, kind="gaussian", sigma=2.0)
+    x = xt.to(DEV)
+    cb = O.calibrate(dtype, _bits_np(xt)[:5000])
+    torch.cuda.synchronize()
+    ref = None
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    noise = torch.randn(4096, 4096, device=DEV)
+    for i in range(5):
+        s = streams[i % 3]
+        with torch.cuda.stream(s):
+            if i == 3:
+                noise = noise @ noise  # concurrent work on the same stream's queue
+            out, nb = sz.compress(x, cb, 0, stream=s)
+        torch.cuda.synchronize()
+        got = out[: int(nb.item())].cpu().numpy()
+        if ref is None:
+            ref = got
+        assert np.array_equal(got, ref), f"run {i} differs"
+
+
+def _corrupt_status(stream_dev, n, dtype, in_bytes=None):
+    y, st = sz.decompress(stream_dev, n, dtype, in_bytes=in_bytes)
+    torch.cuda.synchronize()
+    return int(st.item())
+
+
+def test_corrupt_streams_are_reported():
+    """The decoder validates the stream and reports corruption through the
+    status word; every read stays within in_bytes."""
+    n = 5 * 65536 + 333
+    xt = kvsynth.random_bits(n, O.BF16, seed=8, sigma=2.0)
+    xh = _bits_np(xt)
+    cb = O.calibrate(O.BF16, xh[:2000])
+    good = O.compress(O.BF16, xh, cb)
+    E = u64(good, 16)
+    assert E > 100
+    sec = O.sections(O.BF16, n, 1)
+    dev = torch.from_numpy(good).to(DEV)
+    assert _corrupt_status(dev, n, O.BF16) == 0
+    assert _corrupt_status(dev, n + 1, O.BF16) == O.E_CORRUPT
+    assert _corrupt_status(dev, n, O.E5M2) == O.E_CORRUPT
+    assert _corrupt_status(dev, n, O.BF16, in_bytes=good.size - 1) == O.E_CORRUPT
+
+    def mutated(off, val):
+        t = good.copy()
+        t[off] = val
+        return torch.from_numpy(t).to(DEV)
+
+    assert _corrupt_status(mutated(0, 0x54), n, O.BF16) == O.E_CORRUPT          # magic
+    assert _corrupt_status(mutated(4, 9), n, O.BF16) == O.E_CORRUPT             # version
+    assert _corrupt_status(mutated(55, 1), n, O.BF16) == O.E_CORRUPT            # reserved
+    assert _corrupt_status(mutated(sec["offsets"] + 8 * 2, 0xFF), n, O.BF16) == O.E_CORRUPT  # off[2] > off[3]
+    assert _corrupt_status(mutated(sec["offsets"], 1), n, O.BF16) == O.E_CORRUPT  # off[0] != 0
+    # an escape position beyond the last chunk's length
+    last = sec["esc"] + 3 * (E - 1)
+    assert _corrupt_status(mutated(last + 1, 0xFF), n, O.BF16) == O.E_CORRUPT
+    # two records out of order inside a chunk
+    t = good.copy()
+    t[sec["esc"]:sec["esc"] + 3], t[sec["esc"] + 3:sec["esc"] + 6] = good[sec["esc"] + 3:sec["esc"] + 6], good[sec["esc"]:sec["esc"] + 3]
+    assert _corrupt_status(torch.from_numpy(t).to(DEV), n, O.BF16) == O.E_CORRUPT
+    # the valid stream still decodes exactly afterwards
+    y, st = sz.decompress(dev, n, O.BF16)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and np.array_equal(_bits_np(y), xh)
+
+
+def test_host_argument_errors():
+    x = torch.zeros(1024, dtype=torch.int16, device=DEV)
+    cb = np.arange(16, dtype=np.uint8)
+    with pytest.raises(sz.SplitZipError) as e:
+        sz.compress(x, np.zeros(16, np.uint8))
+    assert e.value.status == sz.E_CODEBOOK
+    small = torch.empty(100, dtype=torch.uint8, device=DEV)
+    with pytest.raises(sz.SplitZipError) as e:
+        sz.compress(x, cb, out=small)
+    assert e.value.status == sz.E_CAPACITY
+    with pytest.raises(sz.SplitZipError) as e:
+        sz.compress(x, np.stack([cb, cb]), segment_elems=1000)
+    assert e.value.status == sz.E_INVALID
+    mis = torch.empty(4096, dtype=torch.uint8, device=DEV)
+    rc = sz.splitzip_compress(sz.BF16, x.data_ptr() + 2, 1000, cb, 1, 0, mis.data_ptr(), mis.numel(), None, None)
+    assert rc == sz.E_INVALID
