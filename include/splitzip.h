@@ -81,7 +81,7 @@ int splitzip_calibrate(int dtype, const void* host_samples, size_t n_elems, uint
 /* Bytes the caller must provide as d_out of splitzip_compress for n_elems
  * elements and n_codebooks codebooks: the largest possible stream (every
  * element escaped) rounded up to 256, plus the encoder's scan workspace
- * (256 + 8 ceil(n_elems / 8192) bytes).  Returns 0 for an invalid dtype,
+ * (16 ceil(n_elems / 8192) bytes).  Returns 0 for an invalid dtype,
  * n_codebooks == 0 or n_elems > 2^40. */
 size_t splitzip_max_compressed_size(int dtype, size_t n_elems, uint32_t n_codebooks);
 

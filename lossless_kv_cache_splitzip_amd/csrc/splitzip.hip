@@ -12,14 +12,16 @@
 //
 // GPU design (ours):
 //   prep kernel   header, codebooks, zero padding, clears the scan workspace.
-//   encode        one pass over the input.  A workgroup of 256 threads owns
-//                 an 8192-element tile: coalesced 16-byte loads, a 256-entry
+//   encode        one pass over the input, one cooperative launch of
+//                 co-resident workgroups, each owning a contiguous block of
+//                 8192-element tiles: coalesced 16-byte loads, a 256-entry
 //                 exponent->code table in LDS, nibble and sign|mantissa
 //                 packing with byte-permute ops, coalesced stores.  Escapes
 //                 are ranked in element order with a wave64 DPP scan and an
-//                 LDS block scan, staged in LDS, and placed by a device-wide
-//                 decoupled look-back over tile aggregates (tile order comes
-//                 from an atomic ticket, so every awaited tile is resident).
+//                 LDS block scan and staged in LDS; per-tile counts are
+//                 scanned across workgroups through flagged words, then
+//                 every tile knows its escape base and its records are
+//                 written.
 //   decode        a workgroup owns a 16384-element tile inside one chunk.  It
 //                 binary-searches its slice of the chunk's escape records,
 //                 stages them in LDS (bitmap + values), then rebuilds values
@@ -44,9 +46,6 @@ constexpr uint32_t kMagic = 0x00315A53u;
 constexpr uint32_t kMaxK = 65535;
 constexpr uint64_t kMaxN = 1ull << 40;
 constexpr int kCbPerPrep = 128;
-constexpr uint64_t kFlagAgg = 1ull << 62;
-constexpr uint64_t kFlagInc = 1ull << 63;
-constexpr uint64_t kValMask = kFlagAgg - 1;
 constexpr uint8_t kEsc = 0x10;  // table entry of an exponent outside the codebook
 
 __host__ __device__ inline uint64_t round256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -67,8 +66,9 @@ __host__ __device__ inline Sections sections_of(int dtype, uint64_t n, uint64_t 
   return s;
 }
 
-// Encoder workspace (ticket + one status word per tile) sits after the
-// largest possible stream.
+// Encoder workspace, after the largest possible stream: a u64 total per
+// round (at most one round per tile), then per tile a u32 escape count and a
+// u32 offset in its round; all flagged words, zeroed before each encode.
 __host__ __device__ inline uint64_t workspace_offset(int dtype, uint64_t n, uint64_t k) {
   return round256(sections_of(dtype, n, k).esc + 3 * n);
 }
@@ -94,33 +94,6 @@ __device__ inline uint32_t wave_inclusive_sum(uint32_t v) {
   carry += row >= 2 ? r1 : 0u;
   carry += row >= 3 ? r2 : 0u;
   return v + carry;
-}
-
-// Decoupled look-back (single thread).  Publishes this tile's aggregate,
-// sums predecessors back to the first inclusive prefix, publishes the
-// inclusive prefix and returns the exclusive one.  A tile only waits on
-// lower tickets, which belong to workgroups already running, and tile 0
-// never waits, so every wait ends.
-__device__ uint64_t look_back(uint64_t* status, uint64_t tile, uint64_t agg) {
-  if (tile == 0) {
-    __hip_atomic_store(&status[0], kFlagInc | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return 0;
-  }
-  __hip_atomic_store(&status[tile], kFlagAgg | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  uint64_t base = 0;
-  uint64_t j = tile - 1;
-  for (;;) {
-    const uint64_t s = __hip_atomic_load(&status[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((s & (kFlagAgg | kFlagInc)) == 0) {
-      __builtin_amdgcn_s_sleep(1);
-      continue;
-    }
-    base += s & kValMask;
-    if (s & kFlagInc) break;
-    --j;
-  }
-  __hip_atomic_store(&status[tile], kFlagInc | (base + agg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return base;
 }
 
 // 4 table entries (code | escape flag << 4), one per byte, for BF16 word pair.
@@ -175,9 +148,8 @@ __device__ inline uint32_t spread4(uint32_t w, int half) {
 struct PrepArgs {
   uint8_t* out;
   uint64_t n, seg_stored, nib, sm, esc, sm_bytes, offsets, chunks;
-  uint64_t* status;
-  uint64_t n_status;
-  uint32_t* ticket;
+  uint64_t* workspace;     // zeroed by prep_kernel
+  uint64_t workspace_words;
   uint64_t* out_bytes;
   uint32_t k, dtype, cb_first, cb_count, main;
   uint8_t cbs[kCbPerPrep * 16];
@@ -187,24 +159,23 @@ __device__ inline void put_le(uint8_t* p, uint64_t v, int bytes) {
   for (int i = 0; i < bytes; ++i) p[i] = (uint8_t)(v >> (8 * i));
 }
 
+// Header, codebooks, zero padding; clears the encoder's workspace.
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   const uint64_t gtid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
   const uint64_t gsize = (uint64_t)gridDim.x * kThreads;
   for (uint64_t i = gtid; i < (uint64_t)a.cb_count * 16; i += gsize)
     a.out[64 + 16 * (uint64_t)a.cb_first + i] = a.cbs[i];
   if (!a.main) return;
-  for (uint64_t i = gtid; i < a.n_status; i += gsize) a.status[i] = 0;
+  for (uint64_t i = gtid; i < a.workspace_words; i += gsize) a.workspace[i] = 0;
   if (blockIdx.x != 0) return;
   const uint32_t t = threadIdx.x;
-  if (t == 0) *a.ticket = 0;
   // zero padding after the offsets, the nibbles and the sign|mantissa bytes
   const uint64_t ends[3] = {a.offsets + 8 * (a.chunks + 1), a.nib + divup(a.n, 2), a.sm + a.sm_bytes};
   const uint64_t stops[3] = {a.nib, a.sm, a.esc};
   for (int r = 0; r < 3; ++r)
     if (ends[r] + t < stops[r]) a.out[ends[r] + t] = 0;
   if (t < 64) {
-    // header: byte t of the 64-byte header
-    uint8_t b = 0;
+    // byte t of the 64-byte header; E and S are final here only when n == 0
     uint64_t v = 0;
     int off = 0;
     if (t < 4) { v = kMagic; off = t; }
@@ -212,12 +183,11 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     else if (t == 6) { v = a.dtype; }
     else if (t == 7) { v = 16; }
     else if (t < 16) { v = a.n; off = t - 8; }
-    else if (t < 32) { v = (a.n == 0 && t >= 24) ? a.esc : 0; off = t & 7; }  // E and S (final when n == 0)
+    else if (t < 32) { v = (a.n == 0 && t >= 24) ? a.esc : 0; off = t & 7; }
     else if (t < 36) { v = a.chunks; off = t - 32; }
     else if (t < 40) { v = a.k; off = t - 36; }
     else if (t < 48) { v = a.seg_stored; off = t - 40; }
-    b = (uint8_t)(v >> (8 * off));
-    a.out[t] = b;
+    a.out[t] = (uint8_t)(v >> (8 * off));
   }
   if (a.n == 0 && t == 0) {
     put_le(a.out + a.offsets, 0, 8);
@@ -226,65 +196,98 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 }
 
 // ---------------------------------------------------------- encode kernels
+//
+// One cooperative launch of G co-resident workgroups.  Tiles are dealt
+// round-robin: in round k workgroup b encodes tile kG + b, so the tiles in
+// flight at any moment are neighbours in memory.
+//   pass 1    for each of its tiles: dense encode (codes, sign|mantissa),
+//             element-order escape ranks; the tile's escape count goes to the
+//             workspace and its escape records are staged in LDS while they
+//             fit.
+//   pass 1.5  workgroup b scans the counts of rounds b, b + G, ...: escape
+//             offset of each tile inside its round, and the round's total.
+//   pass 2    every workgroup walks the rounds in order keeping the running
+//             total of earlier rounds, so each of its tiles knows its global
+//             escape offset; staged records are written there, chunk offsets
+//             and (for the last tile) E and S too.  Tiles whose escapes did
+//             not fit the stage are read again and written directly.
+// Counts, offsets and totals cross workgroups as flagged words; a reader
+// waits only for words whose producer is resident (cooperative launch) and
+// reaches them without waiting itself: pass 1 waits on nothing, pass 1.5 on
+// pass 1 words, pass 2 on pass 1 and 1.5 words.  So every wait ends.
 struct EncArgs {
   const uint8_t* in;
   uint8_t* out;
   uint64_t n, n_tiles, offsets, nib, sm, esc, chunks;
-  uint64_t seg_chunks;  // chunks per codebook segment, 0 when one codebook
-  uint32_t* ticket;
-  uint64_t* status;
+  uint64_t seg_chunks;     // chunks per codebook segment, 0 when one codebook
+  uint32_t* tile_count;    // per tile: escapes in it
+  uint32_t* tile_prefix;   // per tile: escapes before it in its round
+  uint64_t* round_sum;     // per round: escapes in it
   uint64_t* out_bytes;
 };
 
-// Workgroup epilogue shared by both element types: rank -> global record
-// index through the look-back, record stores, chunk offsets, header totals.
-__device__ inline void emit_escapes(const EncArgs& a, uint64_t tile, uint32_t agg, const uint16_t* st_pos,
-                                    const uint8_t* st_val, uint64_t* s_base) {
-  if (threadIdx.x == 0) {
-    const uint64_t base = look_back(a.status, tile, agg);
-    *s_base = base;
-    if ((tile & 7) == 0) put_le(a.out + a.offsets + 8 * (tile >> 3), base, 8);
-    if (tile == a.n_tiles - 1) {
-      const uint64_t e = std::min<uint64_t>(base + agg, a.n);
-      const uint64_t s = a.esc + 3 * e;
-      put_le(a.out + a.offsets + 8 * a.chunks, e, 8);
-      put_le(a.out + 16, e, 8);
-      put_le(a.out + 24, s, 8);
-      if (a.out_bytes) *a.out_bytes = s;
-    }
-  }
+constexpr uint32_t kStage = 8192;  // escape records staged in LDS per workgroup
+
+constexpr uint32_t kPerThread = 8;  // pass 1.5 handles rounds of up to 2048 tiles
+
+struct EncShared {
+  uint16_t st_pos[kStage];
+  uint8_t st_val[kStage];
+  uint8_t table[256];
+  uint32_t wave[8];
+  uint64_t red[4];
+  uint64_t p2_base[kThreads];
+  uint32_t p2_cnt[kThreads];
+  uint32_t p2_at[kThreads];
+};
+
+// Exclusive prefix over the workgroup's threads (thread order) of per-thread
+// u32 values whose sum over any wave fits 32 bits; *total gets the sum.
+__device__ inline uint64_t block_exclusive_sum(EncShared& sh, uint32_t v, uint64_t* total) {
+  const uint32_t inc = wave_inclusive_sum(v);
+  const uint32_t wave = threadIdx.x >> 6;
+  __syncthreads();  // earlier readers of sh.red are done
+  if ((threadIdx.x & 63) == 63) sh.red[wave] = inc;
   __syncthreads();
-  const uint64_t base = *s_base;
-  // a tile holds at most kEncTile escapes and the stream at most n; the
-  // bounds below always hold for a correct scan and keep every store inside
-  // the stream even if they did not
-  const uint32_t lim = (uint32_t)std::min<uint64_t>(std::min<uint64_t>(agg, kEncTile), base < a.n ? a.n - base : 0);
-  for (uint32_t r = threadIdx.x; r < lim; r += kThreads) {
-    uint8_t* d = a.out + a.esc + 3 * (base + r);
-    const uint32_t p = st_pos[r];
-    d[0] = (uint8_t)p;
-    d[1] = (uint8_t)(p >> 8);
-    d[2] = st_val[r];
+  uint64_t pre = 0, tot = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < 4; ++w) {
+    pre += w < wave ? sh.red[w] : 0u;
+    tot += sh.red[w];
   }
+  *total = tot;
+  return pre + inc - v;
 }
 
-__global__ __launch_bounds__(kThreads) void encode_bf16_kernel(EncArgs a) {
-  __shared__ uint8_t table[256];
-  __shared__ uint16_t st_pos[kEncTile];
-  __shared__ uint8_t st_val[kEncTile];
-  __shared__ uint32_t s_wave[2][4];
-  __shared__ uint32_t s_tile;
-  __shared__ uint64_t s_base;
-
+__device__ inline void build_table(const EncArgs& a, EncShared& sh, uint64_t cbi, uint32_t entries) {
   const uint32_t tid = threadIdx.x;
-  if (tid == 0) s_tile = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  table[tid] = kEsc;
+  if (tid < entries) sh.table[tid] = kEsc;
   __syncthreads();
-  const uint64_t tile = s_tile;
-  const uint64_t cbi = a.seg_chunks ? (tile >> 3) / a.seg_chunks : 0;
-  if (tid < 16) table[a.out[64 + 16 * cbi + tid]] = (uint8_t)tid;
+  if (tid < 16) sh.table[a.out[64 + 16 * cbi + tid]] = (uint8_t)tid;
   __syncthreads();
+}
 
+// Per-thread escape bookkeeping of one tile: element-order rank of the
+// thread's first escape in each group, and the escape masks.
+struct TileEsc {
+  uint32_t agg;      // escapes in the tile
+  uint32_t rank[4];  // BF16: per group of 8; E5M2: rank[0] only
+  uint32_t mask[4];  // BF16: 8-bit masks per group; E5M2: mask[0] 32-bit
+};
+
+__device__ inline void wave_totals_to_lds(EncShared& sh, uint32_t i01, uint32_t i23) {
+  const uint32_t wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 63) {
+    sh.wave[wave] = i01;
+    sh.wave[4 + wave] = i23;
+  }
+  __syncthreads();
+}
+
+// BF16 tile: 8192 elements = 4 groups of 2048; thread t owns elements
+// 8t..8t+7 of each group (16-byte loads, coalesced per wave).
+__device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t tile, bool store) {
+  const uint32_t tid = threadIdx.x;
   const uint64_t first = tile * kEncTile;
   const uint16_t* in16 = reinterpret_cast<const uint16_t*>(a.in);
   uint4 w[4];
@@ -307,82 +310,80 @@ __global__ __launch_bounds__(kThreads) void encode_bf16_kernel(EncArgs a) {
       w[g] = make_uint4(v0, v1, v2, v3);
     }
   }
-
-  uint32_t codes_lo[4], codes_hi[4], cnt[4];
+  TileEsc r;
+  uint32_t cnt[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const uint4 x = w[g];
-    uint32_t lo = gather4(table[(x.x >> 7) & 0xFF], table[(x.x >> 23) & 0xFF], table[(x.y >> 7) & 0xFF],
-                          table[(x.y >> 23) & 0xFF]);
-    uint32_t hi = gather4(table[(x.z >> 7) & 0xFF], table[(x.z >> 23) & 0xFF], table[(x.w >> 7) & 0xFF],
-                          table[(x.w >> 23) & 0xFF]);
+    const uint8_t* tb = sh.table;
+    uint32_t lo = gather4(tb[(x.x >> 7) & 0xFF], tb[(x.x >> 23) & 0xFF], tb[(x.y >> 7) & 0xFF], tb[(x.y >> 23) & 0xFF]);
+    uint32_t hi = gather4(tb[(x.z >> 7) & 0xFF], tb[(x.z >> 23) & 0xFF], tb[(x.w >> 7) & 0xFF], tb[(x.w >> 23) & 0xFF]);
     if (valid[g] < 8) {
       lo &= keep_low_bytes(valid[g]);
       hi &= valid[g] > 4 ? keep_low_bytes(valid[g] - 4) : 0u;
     }
-    codes_lo[g] = lo;
-    codes_hi[g] = hi;
-    cnt[g] = __builtin_popcount(lo & 0x10101010u) + __builtin_popcount(hi & 0x10101010u);
-
-    const uint32_t nib = pack_nibbles(lo, hi);
-    // sign|mantissa: high bytes and low bytes of the four BF16 pairs
-    const uint32_t h01 = perm(x.y, x.x, 0x07050301u), l01 = perm(x.y, x.x, 0x06040200u);
-    const uint32_t h23 = perm(x.w, x.z, 0x07050301u), l23 = perm(x.w, x.z, 0x06040200u);
-    const uint32_t sm0 = (h01 & 0x80808080u) | (l01 & 0x7F7F7F7Fu);
-    const uint32_t sm1 = (h23 & 0x80808080u) | (l23 & 0x7F7F7F7Fu);
-    const uint64_t e0 = first + g * 2048 + 8 * tid;
-    if (valid[g] == 8) {
-      *reinterpret_cast<uint32_t*>(a.out + a.nib + e0 / 2) = nib;
-      *reinterpret_cast<uint2*>(a.out + a.sm + e0) = make_uint2(sm0, sm1);
-    } else if (valid[g] > 0) {
-      for (uint32_t b = 0; b < (valid[g] + 1) / 2; ++b) a.out[a.nib + e0 / 2 + b] = (uint8_t)(nib >> (8 * b));
-      for (uint32_t j = 0; j < valid[g]; ++j)
-        a.out[a.sm + e0 + j] = (uint8_t)((j < 4 ? sm0 : sm1) >> (8 * (j & 3)));
+    r.mask[g] = flag_mask4(lo) | (flag_mask4(hi) << 4);
+    cnt[g] = __builtin_popcount(r.mask[g]);
+    if (store) {
+      const uint32_t nib = pack_nibbles(lo, hi);
+      // sign|mantissa: high bytes and low bytes of the four BF16 pairs
+      const uint32_t h01 = perm(x.y, x.x, 0x07050301u), l01 = perm(x.y, x.x, 0x06040200u);
+      const uint32_t h23 = perm(x.w, x.z, 0x07050301u), l23 = perm(x.w, x.z, 0x06040200u);
+      const uint32_t sm0 = (h01 & 0x80808080u) | (l01 & 0x7F7F7F7Fu);
+      const uint32_t sm1 = (h23 & 0x80808080u) | (l23 & 0x7F7F7F7Fu);
+      const uint64_t e0 = first + g * 2048 + 8 * tid;
+      if (valid[g] == 8) {
+        *reinterpret_cast<uint32_t*>(a.out + a.nib + e0 / 2) = nib;
+        *reinterpret_cast<uint2*>(a.out + a.sm + e0) = make_uint2(sm0, sm1);
+      } else if (valid[g] > 0) {
+        for (uint32_t b = 0; b < (valid[g] + 1) / 2; ++b) a.out[a.nib + e0 / 2 + b] = (uint8_t)(nib >> (8 * b));
+        for (uint32_t j = 0; j < valid[g]; ++j) a.out[a.sm + e0 + j] = (uint8_t)((j < 4 ? sm0 : sm1) >> (8 * (j & 3)));
+      }
     }
   }
-
   // element-order ranks: groups are ordered (g, thread), so scan the four
   // per-thread counts as 16-bit fields (a group holds at most 2048 escapes)
   const uint32_t p01 = cnt[0] | (cnt[1] << 16), p23 = cnt[2] | (cnt[3] << 16);
   const uint32_t i01 = wave_inclusive_sum(p01), i23 = wave_inclusive_sum(p23);
+  wave_totals_to_lds(sh, i01, i23);
   const uint32_t wave = tid >> 6;
-  if ((tid & 63) == 63) {
-    s_wave[0][wave] = i01;
-    s_wave[1][wave] = i23;
-  }
-  __syncthreads();
   uint32_t pre01 = 0, pre23 = 0, tot01 = 0, tot23 = 0;
 #pragma unroll
   for (uint32_t v = 0; v < 4; ++v) {
-    const uint32_t x = s_wave[0][v], y = s_wave[1][v];
+    const uint32_t x = sh.wave[v], y = sh.wave[4 + v];
     pre01 += v < wave ? x : 0u;
     pre23 += v < wave ? y : 0u;
     tot01 += x;
     tot23 += y;
   }
   const uint32_t g0 = tot01 & 0xFFFF, g1 = tot01 >> 16, g2 = tot23 & 0xFFFF, g3 = tot23 >> 16;
-  const uint32_t agg = g0 + g1 + g2 + g3;
+  r.agg = g0 + g1 + g2 + g3;
   const uint32_t x01 = pre01 + i01 - p01, x23 = pre23 + i23 - p23;
-  uint32_t rank[4] = {x01 & 0xFFFF, g0 + (x01 >> 16), g0 + g1 + (x23 & 0xFFFF), g0 + g1 + g2 + (x23 >> 16)};
+  r.rank[0] = x01 & 0xFFFF;
+  r.rank[1] = g0 + (x01 >> 16);
+  r.rank[2] = g0 + g1 + (x23 & 0xFFFF);
+  r.rank[3] = g0 + g1 + g2 + (x23 >> 16);
+  return r;
+}
 
+// The escapes of one BF16 tile: position in chunk and raw exponent, handed
+// to `put(rank, pos, exponent)` in element order.
+template <typename Put>
+__device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put) {
+  const uint32_t tid = threadIdx.x;
+  const uint16_t* in16 = reinterpret_cast<const uint16_t*>(a.in);
   const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTile;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    if (cnt[g] == 0) continue;
-    uint32_t r = rank[g];
-    uint32_t m = flag_mask4(codes_lo[g]) | (flag_mask4(codes_hi[g]) << 4);
-    const uint64_t e0 = first + g * 2048 + 8 * tid;
-    while (m) {  // escaped elements of this group, in element order
+    uint32_t m = r.mask[g];
+    uint32_t k = r.rank[g];
+    const uint64_t e0 = tile * kEncTile + g * 2048 + 8 * tid;
+    while (m) {
       const uint32_t j = __builtin_ctz(m);
       m &= m - 1;
-      if (r < kEncTile) {
-        st_pos[r] = (uint16_t)(in_chunk + g * 2048 + 8 * tid + j);
-        st_val[r] = (uint8_t)(in16[e0 + j] >> 7);
-      }
-      ++r;
+      put(k++, in_chunk + g * 2048 + 8 * tid + j, (uint32_t)(in16[e0 + j] >> 7) & 0xFF);
     }
   }
-  emit_escapes(a, tile, agg, st_pos, st_val, &s_base);
 }
 
 // E5M2: a thread owns 32 consecutive elements (32 input bytes, 16 nibble
@@ -390,27 +391,12 @@ __global__ __launch_bounds__(kThreads) void encode_bf16_kernel(EncArgs a) {
 __device__ inline uint32_t signmant12(uint32_t w) {
   // byte k -> 3-bit value sign<<2 | mantissa, then 4 x 3 bits -> 12 bits
   const uint32_t u = ((w >> 5) & 0x04040404u) | (w & 0x03030303u);
-  const uint32_t v = u | (u >> 5);          // bits 0..5: e0|e1<<3 ; bits 16..21: e2|e3<<3
+  const uint32_t v = u | (u >> 5);  // bits 0..5: e0|e1<<3 ; bits 16..21: e2|e3<<3
   return (v & 0x3Fu) | ((v >> 10) & 0xFC0u);
 }
 
-__global__ __launch_bounds__(kThreads) void encode_e5m2_kernel(EncArgs a) {
-  __shared__ uint8_t table[32];
-  __shared__ uint16_t st_pos[kEncTile];
-  __shared__ uint8_t st_val[kEncTile];
-  __shared__ uint32_t s_wave[4];
-  __shared__ uint32_t s_tile;
-  __shared__ uint64_t s_base;
-
+__device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t tile, bool store) {
   const uint32_t tid = threadIdx.x;
-  if (tid == 0) s_tile = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (tid < 32) table[tid] = kEsc;
-  __syncthreads();
-  const uint64_t tile = s_tile;
-  const uint64_t cbi = a.seg_chunks ? (tile >> 3) / a.seg_chunks : 0;
-  if (tid < 16) table[a.out[64 + 16 * cbi + tid]] = (uint8_t)tid;
-  __syncthreads();
-
   const uint64_t e0 = tile * kEncTile + 32 * tid;
   const uint32_t valid = e0 >= a.n ? 0u : (uint32_t)std::min<uint64_t>(32, a.n - e0);
   uint32_t w[8];
@@ -427,70 +413,240 @@ __global__ __launch_bounds__(kThreads) void encode_e5m2_kernel(EncArgs a) {
     }
   }
   uint32_t codes[8];
-  uint32_t cnt = 0;
+  TileEsc r;
+  r.mask[0] = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const uint32_t x = w[k];
-    uint32_t c = gather4(table[(x >> 2) & 0x1F], table[(x >> 10) & 0x1F], table[(x >> 18) & 0x1F],
-                         table[(x >> 26) & 0x1F]);
-    if (valid < 32) {
-      const uint32_t have = valid > 4u * k ? valid - 4u * k : 0u;
-      c &= keep_low_bytes(have);
-    }
+    const uint8_t* tb = sh.table;
+    uint32_t c = gather4(tb[(x >> 2) & 0x1F], tb[(x >> 10) & 0x1F], tb[(x >> 18) & 0x1F], tb[(x >> 26) & 0x1F]);
+    if (valid < 32) c &= keep_low_bytes(valid > 4u * k ? valid - 4u * k : 0u);
     codes[k] = c;
-    cnt += __builtin_popcount(c & 0x10101010u);
+    r.mask[0] |= flag_mask4(c) << (4 * k);
   }
-  uint32_t nib[4];
+  const uint32_t cnt = __builtin_popcount(r.mask[0]);
+  if (store) {
+    uint32_t nib[4];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) nib[d] = pack_nibbles(codes[2 * d], codes[2 * d + 1]);
-  uint32_t g24[4];
+    for (int d = 0; d < 4; ++d) nib[d] = pack_nibbles(codes[2 * d], codes[2 * d + 1]);
+    uint32_t g24[4];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) g24[d] = signmant12(w[2 * d]) | (signmant12(w[2 * d + 1]) << 12);
-  const uint32_t s0 = g24[0] | (g24[1] << 24);
-  const uint32_t s1 = (g24[1] >> 8) | (g24[2] << 16);
-  const uint32_t s2 = (g24[2] >> 16) | (g24[3] << 8);
-  const uint64_t smo = a.sm + 3 * (e0 / 8);
-  if (valid == 32) {
-    *reinterpret_cast<uint4*>(a.out + a.nib + e0 / 2) = make_uint4(nib[0], nib[1], nib[2], nib[3]);
-    uint32_t* sp = reinterpret_cast<uint32_t*>(a.out + smo);
-    sp[0] = s0;
-    sp[1] = s1;
-    sp[2] = s2;
-  } else if (valid > 0) {
-    for (uint32_t b = 0; b < (valid + 1) / 2; ++b)
-      a.out[a.nib + e0 / 2 + b] = (uint8_t)(pick4(nib[0], nib[1], nib[2], nib[3], b >> 2) >> (8 * (b & 3)));
-    for (uint32_t b = 0; b < 3 * ((valid + 7) / 8); ++b)
-      a.out[smo + b] = (uint8_t)(pick4(s0, s1, s2, 0u, b >> 2) >> (8 * (b & 3)));
+    for (int d = 0; d < 4; ++d) g24[d] = signmant12(w[2 * d]) | (signmant12(w[2 * d + 1]) << 12);
+    const uint32_t s0 = g24[0] | (g24[1] << 24);
+    const uint32_t s1 = (g24[1] >> 8) | (g24[2] << 16);
+    const uint32_t s2 = (g24[2] >> 16) | (g24[3] << 8);
+    const uint64_t smo = a.sm + 3 * (e0 / 8);
+    if (valid == 32) {
+      *reinterpret_cast<uint4*>(a.out + a.nib + e0 / 2) = make_uint4(nib[0], nib[1], nib[2], nib[3]);
+      uint32_t* sp = reinterpret_cast<uint32_t*>(a.out + smo);
+      sp[0] = s0;
+      sp[1] = s1;
+      sp[2] = s2;
+    } else if (valid > 0) {
+      for (uint32_t b = 0; b < (valid + 1) / 2; ++b)
+        a.out[a.nib + e0 / 2 + b] = (uint8_t)(pick4(nib[0], nib[1], nib[2], nib[3], b >> 2) >> (8 * (b & 3)));
+      for (uint32_t b = 0; b < 3 * ((valid + 7) / 8); ++b)
+        a.out[smo + b] = (uint8_t)(pick4(s0, s1, s2, 0u, b >> 2) >> (8 * (b & 3)));
+    }
   }
-
   const uint32_t inc = wave_inclusive_sum(cnt);
+  wave_totals_to_lds(sh, inc, 0);
   const uint32_t wave = tid >> 6;
-  if ((tid & 63) == 63) s_wave[wave] = inc;
-  __syncthreads();
   uint32_t pre = 0, agg = 0;
 #pragma unroll
   for (uint32_t v = 0; v < 4; ++v) {
-    pre += v < wave ? s_wave[v] : 0u;
-    agg += s_wave[v];
+    pre += v < wave ? sh.wave[v] : 0u;
+    agg += sh.wave[v];
   }
-  if (cnt) {
-    uint32_t r = pre + inc - cnt;
-    const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTile + 32 * tid;
-    uint32_t m = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) m |= flag_mask4(codes[k]) << (4 * k);
-    while (m) {  // escaped elements, in element order
-      const uint32_t j = __builtin_ctz(m);
-      m &= m - 1;
-      if (r < kEncTile) {
-        st_pos[r] = (uint16_t)(in_chunk + j);
-        st_val[r] = (uint8_t)((a.in[e0 + j] >> 2) & 0x1F);
-      }
-      ++r;
-    }
-  }
-  emit_escapes(a, tile, agg, st_pos, st_val, &s_base);
+  r.agg = agg;
+  r.rank[0] = pre + inc - cnt;
+  return r;
 }
+
+template <typename Put>
+__device__ inline void for_each_escape_e5m2(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put) {
+  const uint32_t tid = threadIdx.x;
+  const uint64_t e0 = tile * kEncTile + 32 * tid;
+  const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTile + 32 * tid;
+  uint32_t m = r.mask[0];
+  uint32_t k = r.rank[0];
+  while (m) {
+    const uint32_t j = __builtin_ctz(m);
+    m &= m - 1;
+    put(k++, in_chunk + j, (uint32_t)(a.in[e0 + j] >> 2) & 0x1F);
+  }
+}
+
+__device__ inline void put_record(const EncArgs& a, uint64_t index, uint32_t pos, uint32_t val) {
+  if (index >= a.n) return;  // never taken for a correct scan; keeps stores inside the stream
+  uint8_t* d = a.out + a.esc + 3 * index;
+  d[0] = (uint8_t)pos;
+  d[1] = (uint8_t)(pos >> 8);
+  d[2] = (uint8_t)val;
+}
+
+// Cross-workgroup words carry a valid flag in the same atomic word, so a
+// relaxed agent-scope load that sees the flag also sees the value: no fence
+// (on this GPU an agent-scope fence writes back or invalidates the XCD's L2).
+constexpr uint32_t kValid32 = 1u << 31;
+constexpr uint64_t kValid64 = 1ull << 63;
+
+__device__ inline void publish32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v | kValid32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void publish64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v | kValid64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t peek32(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t peek64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait for a published word; the caller's workgroup is resident and so is
+// its producer, which publishes without waiting on anything this one holds.
+__device__ inline uint32_t await32(const uint32_t* p) {
+  uint32_t v;
+  while (!((v = peek32(p)) & kValid32)) __builtin_amdgcn_s_sleep(4);
+  return v & ~kValid32;
+}
+__device__ inline uint64_t await64(const uint64_t* p) {
+  uint64_t v;
+  while (!((v = peek64(p)) & kValid64)) __builtin_amdgcn_s_sleep(4);
+  return v & ~kValid64;
+}
+
+template <bool kBf16>
+__device__ void encode_rounds(const EncArgs& a) {
+  __shared__ EncShared sh;
+  const uint32_t tid = threadIdx.x;
+  const uint64_t G = gridDim.x, b = blockIdx.x;
+  const uint64_t rounds = divup(a.n_tiles, G);
+  const uint32_t entries = kBf16 ? 256u : 32u;
+  uint64_t table_cb = ~0ull;
+  uint32_t staged = 0;        // records in the LDS stage (same value in every thread)
+  uint64_t spill = rounds;    // first round whose records are not staged
+
+  // ---- pass 1
+  for (uint64_t k = 0; k < rounds; ++k) {
+    const uint64_t t = k * G + b;
+    if (t >= a.n_tiles) break;
+    const uint64_t cbi = a.seg_chunks ? (t >> 3) / a.seg_chunks : 0;
+    if (cbi != table_cb) {
+      build_table(a, sh, cbi, entries);
+      table_cb = cbi;
+    }
+    const TileEsc r = kBf16 ? encode_tile_bf16(a, sh, t, true) : encode_tile_e5m2(a, sh, t, true);
+    if (tid == 0) publish32(&a.tile_count[t], r.agg);
+    if (spill == rounds && staged + r.agg <= kStage) {
+      const uint32_t at = staged;
+      auto stage = [&](uint32_t i, uint32_t pos, uint32_t val) {
+        sh.st_pos[at + i] = (uint16_t)pos;
+        sh.st_val[at + i] = (uint8_t)val;
+      };
+      if (kBf16) for_each_escape_bf16(a, t, r, stage);
+      else for_each_escape_e5m2(a, t, r, stage);
+      staged += r.agg;
+    } else if (spill == rounds) {
+      spill = k;
+    }
+    __syncthreads();  // the wave totals in LDS are reused by the next tile
+  }
+
+  // ---- pass 1.5: scan of the counts of rounds b, b + G, ...; thread i
+  // takes a run of consecutive tiles of the round, all loads issued at once
+  const uint32_t per = (uint32_t)divup(G, kThreads);  // tiles per thread (<= kPerThread)
+  for (uint64_t k = b; k < rounds; k += G) {
+    const uint64_t t0 = k * G + (uint64_t)tid * per, t1 = std::min<uint64_t>((k + 1) * G, a.n_tiles);
+    uint32_t c[kPerThread];
+    uint32_t mine = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kPerThread; ++j)  // issue every load, then wait for stragglers
+      c[j] = (j < per && t0 + j < t1) ? peek32(&a.tile_count[t0 + j]) : kValid32;
+#pragma unroll
+    for (uint32_t j = 0; j < kPerThread; ++j) {
+      if (!(c[j] & kValid32)) c[j] = await32(&a.tile_count[t0 + j]);
+      c[j] &= ~kValid32;
+      mine += c[j];
+    }
+    uint64_t total;
+    uint32_t run = (uint32_t)block_exclusive_sum(sh, mine, &total);
+#pragma unroll
+    for (uint32_t j = 0; j < kPerThread; ++j) {
+      if (j < per && t0 + j < t1) publish32(&a.tile_prefix[t0 + j], run);
+      run += c[j];
+    }
+    if (tid == 0) publish64(&a.round_sum[k], total);
+  }
+
+  // ---- pass 2, 256 rounds at a time: thread i loads round k0 + i's total
+  // and this workgroup's tile of that round; block scans give every tile its
+  // global escape offset and its place in the LDS stage.
+  uint64_t before = 0;  // escapes in rounds before k0
+  uint32_t at = 0;      // staged records of tiles before round k0
+  for (uint64_t k0 = 0; k0 < rounds; k0 += kThreads) {
+    const uint64_t k = k0 + tid;
+    const uint64_t t = k * G + b;
+    uint32_t rsum = 0, cnt = 0, tpre = 0;
+    if (k < rounds) {
+      uint64_t r64 = peek64(&a.round_sum[k]);
+      if (t < a.n_tiles) {
+        cnt = peek32(&a.tile_count[t]);
+        tpre = peek32(&a.tile_prefix[t]);
+        cnt = (cnt & kValid32) ? cnt & ~kValid32 : await32(&a.tile_count[t]);
+        tpre = (tpre & kValid32) ? tpre & ~kValid32 : await32(&a.tile_prefix[t]);
+      }
+      rsum = (uint32_t)((r64 & kValid64) ? r64 & ~kValid64 : await64(&a.round_sum[k]));
+    }
+    uint64_t rtotal, ctotal;
+    const uint64_t rpre = block_exclusive_sum(sh, rsum, &rtotal);
+    const uint64_t cpre = block_exclusive_sum(sh, k < spill ? cnt : 0u, &ctotal);
+    const uint64_t base = before + rpre + tpre;
+    if (k < rounds && t < a.n_tiles) {
+      if ((t & 7) == 0) put_le(a.out + a.offsets + 8 * (t >> 3), base, 8);
+      if (t == a.n_tiles - 1) {
+        const uint64_t e = std::min<uint64_t>(base + cnt, a.n);
+        const uint64_t s = a.esc + 3 * e;
+        put_le(a.out + a.offsets + 8 * a.chunks, e, 8);
+        put_le(a.out + 16, e, 8);
+        put_le(a.out + 24, s, 8);
+        if (a.out_bytes) *a.out_bytes = s;
+      }
+    }
+    sh.p2_base[tid] = base;
+    sh.p2_cnt[tid] = cnt;
+    sh.p2_at[tid] = at + (uint32_t)cpre;
+    __syncthreads();
+    const uint32_t batch = (uint32_t)std::min<uint64_t>(kThreads, rounds - k0);
+    for (uint32_t i = 0; i < batch; ++i) {
+      const uint64_t kk = k0 + i, tt = kk * G + b;
+      if (tt >= a.n_tiles) break;
+      const uint64_t tb = sh.p2_base[i];
+      if (kk < spill) {
+        const uint32_t n_i = sh.p2_cnt[i], a_i = sh.p2_at[i];
+        for (uint32_t r = tid; r < n_i; r += kThreads) put_record(a, tb + r, sh.st_pos[a_i + r], sh.st_val[a_i + r]);
+      } else {
+        // not staged: read the tile again and write its records directly
+        const uint64_t cbi = a.seg_chunks ? (tt >> 3) / a.seg_chunks : 0;
+        if (cbi != table_cb) {
+          build_table(a, sh, cbi, entries);
+          table_cb = cbi;
+        }
+        const TileEsc r = kBf16 ? encode_tile_bf16(a, sh, tt, false) : encode_tile_e5m2(a, sh, tt, false);
+        auto direct = [&](uint32_t j, uint32_t pos, uint32_t val) { put_record(a, tb + j, pos, val); };
+        if (kBf16) for_each_escape_bf16(a, tt, r, direct);
+        else for_each_escape_e5m2(a, tt, r, direct);
+        __syncthreads();
+      }
+    }
+    before += rtotal;
+    at += (uint32_t)ctotal;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void encode_bf16_kernel(EncArgs a) { encode_rounds<true>(a); }
+__global__ __launch_bounds__(kThreads) void encode_e5m2_kernel(EncArgs a) { encode_rounds<false>(a); }
 
 // ---------------------------------------------------------- decode kernels
 struct DecArgs {
@@ -628,7 +784,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
   const uint64_t first = tile * kDecTile;
   const uint8_t* bm8 = reinterpret_cast<const uint8_t*>(bitmap);
   uint16_t* out16 = reinterpret_cast<uint16_t*>(a.out);
-#pragma unroll 2
+  #pragma unroll 2
   for (int g = 0; g < 8; ++g) {
     const uint32_t local = g * 2048 + 8 * tid;
     const uint64_t e0 = first + local;
@@ -662,7 +818,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
       else e_hi = (e_hi & ~(0xFFu << sh)) | (v << sh);
     }
     uint32_t o[4];
-#pragma unroll
+    #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const uint32_t e = half ? e_hi : e_lo;
       const uint32_t m = half ? sm.y : sm.x;
@@ -709,7 +865,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
   }
   const uint32_t tid = threadIdx.x;
   const uint64_t first = tile * kDecTile;
-#pragma unroll 1
+  #pragma unroll 1
   for (int g = 0; g < 2; ++g) {
     const uint32_t local = g * 8192 + 32 * tid;
     const uint64_t e0 = first + local;
@@ -725,12 +881,12 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
       sw[2] = ld32(a.in + smo + 8);
     } else {
       const uint32_t nb = (valid + 1) / 2, sb = 3 * ((valid + 7) / 8);
-#pragma unroll
+      #pragma unroll
       for (int k = 0; k < 4; ++k) {
         nib[k] = 0;
         for (uint32_t b = 0; b < 4 && 4 * k + b < nb; ++b) nib[k] |= (uint32_t)a.in[h.s.nib + e0 / 2 + 4 * k + b] << (8 * b);
       }
-#pragma unroll
+      #pragma unroll
       for (int k = 0; k < 3; ++k) {
         sw[k] = 0;
         for (uint32_t b = 0; b < 4 && 4 * k + b < sb; ++b) sw[k] |= (uint32_t)a.in[smo + 4 * k + b] << (8 * b);
@@ -738,7 +894,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
     }
     const uint32_t esc_bits = bitmap[local >> 5];
     uint32_t o[8];
-#pragma unroll
+    #pragma unroll
     for (int k = 0; k < 8; ++k) {
       uint32_t e = lut4(spread4(nib[k >> 1], k & 1), l0, l1, l2, l3);
       uint32_t mk = (esc_bits >> (4 * k)) & 0xFu;
@@ -761,7 +917,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
       *reinterpret_cast<uint4*>(a.out + e0) = make_uint4(o[0], o[1], o[2], o[3]);
       *reinterpret_cast<uint4*>(a.out + e0 + 16) = make_uint4(o[4], o[5], o[6], o[7]);
     } else {
-#pragma unroll
+      #pragma unroll
       for (int k = 0; k < 8; ++k)
         for (uint32_t b = 0; b < 4 && 4 * k + b < valid; ++b) a.out[e0 + 4 * k + b] = (uint8_t)(o[k] >> (8 * b));
     }
@@ -813,7 +969,7 @@ int splitzip_calibrate(int dtype, const void* host_samples, size_t n_elems, uint
 
 size_t splitzip_max_compressed_size(int dtype, size_t n_elems, uint32_t n_codebooks) {
   if (!dtype_valid(dtype) || n_codebooks == 0 || n_codebooks > kMaxK || n_elems > kMaxN) return 0;
-  return workspace_offset(dtype, n_elems, n_codebooks) + 256 + 8 * divup(n_elems, kEncTile);
+  return workspace_offset(dtype, n_elems, n_codebooks) + 16 * divup(n_elems, kEncTile);
 }
 
 int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks, uint32_t n_codebooks,
@@ -834,8 +990,9 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
   const uint64_t n_tiles = divup(n, kEncTile);
   uint8_t* out = static_cast<uint8_t*>(d_out);
   const uint64_t ws = workspace_offset(dtype, n, n_codebooks);
-  uint32_t* ticket = reinterpret_cast<uint32_t*>(out + ws);
-  uint64_t* status = reinterpret_cast<uint64_t*>(out + ws + 256);
+  uint64_t* round_sum = reinterpret_cast<uint64_t*>(out + ws);  // at most n_tiles rounds
+  uint32_t* tile_count = reinterpret_cast<uint32_t*>(round_sum + n_tiles);
+  uint32_t* tile_prefix = tile_count + n_tiles;
 
   for (uint32_t first = 0; first < n_codebooks; first += kCbPerPrep) {
     PrepArgs p;
@@ -849,9 +1006,8 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
     p.sm_bytes = s.sm_bytes;
     p.offsets = s.offsets;
     p.chunks = s.chunks;
-    p.status = status;
-    p.n_status = n_tiles;
-    p.ticket = ticket;
+    p.workspace = round_sum;
+    p.workspace_words = 2 * n_tiles;
     p.out_bytes = d_out_bytes;
     p.k = n_codebooks;
     p.dtype = (uint32_t)dtype;
@@ -859,8 +1015,8 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
     p.cb_count = std::min<uint32_t>(kCbPerPrep, n_codebooks - first);
     p.main = first == 0;
     memcpy(p.cbs, h_codebooks + 16ull * first, 16ull * p.cb_count);
-    const uint64_t work = std::max<uint64_t>(p.main ? n_tiles : 0, 16ull * p.cb_count);
-    const uint32_t blocks = (uint32_t)std::min<uint64_t>(1024, std::max<uint64_t>(1, divup(work, kThreads)));
+    const uint64_t work = std::max<uint64_t>(p.main ? divup(p.workspace_words, 4) : 0, 16ull * p.cb_count);
+    const uint32_t blocks = (uint32_t)std::min<uint64_t>(2048, std::max<uint64_t>(1, divup(work, kThreads)));
     prep_kernel<<<blocks, kThreads, 0, stream>>>(p);
     if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
   }
@@ -877,14 +1033,25 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
   e.esc = s.esc;
   e.chunks = s.chunks;
   e.seg_chunks = n_codebooks == 1 ? 0 : segment_elems / kChunk;
-  e.ticket = ticket;
-  e.status = status;
+  e.tile_count = tile_count;
+  e.tile_prefix = tile_prefix;
+  e.round_sum = round_sum;
   e.out_bytes = d_out_bytes;
-  if (dtype == SPLITZIP_BF16)
-    encode_bf16_kernel<<<(uint32_t)n_tiles, kThreads, 0, stream>>>(e);
-  else
-    encode_e5m2_kernel<<<(uint32_t)n_tiles, kThreads, 0, stream>>>(e);
-  if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
+  const void* kernel = dtype == SPLITZIP_BF16 ? reinterpret_cast<const void*>(&encode_bf16_kernel)
+                                              : reinterpret_cast<const void*>(&encode_e5m2_kernel);
+  // the waits need every workgroup resident: a cooperative launch of at most
+  // the number of co-resident workgroups, and at most one per tile
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || cus <= 0 ||
+      per_cu <= 0)
+    return SPLITZIP_E_HIP;
+  const uint32_t grid = (uint32_t)std::min<uint64_t>(
+      std::min<uint64_t>(n_tiles, (uint64_t)cus * (uint64_t)per_cu), (uint64_t)kThreads * kPerThread);
+  void* args[] = {&e};
+  if (hipLaunchCooperativeKernel(kernel, dim3(grid), dim3(kThreads), args, 0, stream) != hipSuccess)
+    return SPLITZIP_E_HIP;
   return SPLITZIP_OK;
 }
 
