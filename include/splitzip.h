@@ -80,8 +80,9 @@ int splitzip_calibrate(int dtype, const void* host_samples, size_t n_elems, uint
 
 /* Bytes the caller must provide as d_out of splitzip_compress for n_elems
  * elements and n_codebooks codebooks: the largest possible stream (every
- * element escaped) rounded up to 256, plus the encoder's scan workspace
- * (16 ceil(n_elems / 8192) bytes).  Returns 0 for an invalid dtype,
+ * element escaped) rounded up to 256, plus the encoder's workspace: per 8192-element tile 2052 bytes (a count
+ * and a staging slot for up to 512 escape records) and per 64 tiles 8
+ * bytes, with 256-byte alignment.  Returns 0 for an invalid dtype,
  * n_codebooks == 0 or n_elems > 2^40. */
 size_t splitzip_max_compressed_size(int dtype, size_t n_elems, uint32_t n_codebooks);
 
@@ -110,15 +111,18 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
 /* Decode (technical summary, "Estrategia de Decodificacion / Paralelismo"
  * and "Correccion"; English explainer, "4. Why It's Fast"): map every 4-bit
  * code through its codebook, recombine with the sign|mantissa bits, then
- * overwrite the exponent of every escaped element with its raw value.
+ * overwrite the exponent of every escaped element with its raw value.  One
+ * kernel launch.
  *   d_in      the stream (in_bytes >= its size S, 16-byte aligned).
  *   dtype, n_elems must match the stream header.
  *   d_out     n_elems elements, 16-byte aligned.
- *   d_status  optional (may be NULL), device int32: set to SPLITZIP_OK, then
- *             to SPLITZIP_E_CORRUPT if the GPU finds the stream invalid (bad
+ *   d_status  optional (may be NULL), device int32, sticky: the caller sets
+ *             it to SPLITZIP_OK (0) beforehand; the GPU writes
+ *             SPLITZIP_E_CORRUPT into it if it finds the stream invalid (bad
  *             magic, version, dtype, n, sizes, codebook range, non-monotone
- *             chunk offsets, escape positions out of range or out of order).
- *             d_out is then unspecified.  Every read stays inside in_bytes.
+ *             chunk offsets, escape positions out of range or out of order)
+ *             and never clears it, so one word can watch many calls.  d_out
+ *             is then unspecified.  Every read stays inside in_bytes.
  * Returns SPLITZIP_OK, SPLITZIP_E_INVALID or SPLITZIP_E_HIP. */
 int splitzip_decompress(const void* d_in, size_t in_bytes, int dtype, size_t n_elems, void* d_out,
                         int32_t* d_status, hipStream_t stream);

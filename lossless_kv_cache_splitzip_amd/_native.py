@@ -160,8 +160,9 @@ def compress(x, codebooks, segment_elems: int = 0, out=None, out_bytes=None, str
 def decompress(stream_buf, n_elems: int, dtype: int, out=None, status=None, in_bytes: int | None = None,
                stream=None):
     """Decompress a stream held in a uint8 device tensor.  Returns ``(out,
-    status)`` where ``status`` is a one-element int32 device tensor (0, or
-    E_CORRUPT).  Nothing is synchronized."""
+    status)`` where ``status`` is a one-element int32 device tensor: 0, or
+    E_CORRUPT once a corrupt stream was seen (a passed-in ``status`` is not
+    cleared first).  Nothing is synchronized."""
     import torch
     if not stream_buf.is_cuda or not stream_buf.is_contiguous():
         raise ValueError("stream must be a contiguous device tensor")

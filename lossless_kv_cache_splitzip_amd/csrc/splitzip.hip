@@ -66,11 +66,32 @@ __host__ __device__ inline Sections sections_of(int dtype, uint64_t n, uint64_t 
   return s;
 }
 
-// Encoder workspace, after the largest possible stream: a u64 total per
-// round (at most one round per tile), then per tile a u32 escape count and a
-// u32 offset in its round; all flagged words, zeroed before each encode.
+// Encoder workspace, after the largest possible stream: u64 escapes per
+// block of 64 tiles, u32 escapes per tile, then per tile a staging slot of
+// 512 u32 records.
 __host__ __device__ inline uint64_t workspace_offset(int dtype, uint64_t n, uint64_t k) {
   return round256(sections_of(dtype, n, k).esc + 3 * n);
+}
+
+struct Workspace {
+  uint64_t* block_sum;
+  uint32_t* tile_count;
+  uint32_t* stage;
+  uint64_t end;  // bytes from the stream start
+};
+
+__host__ inline Workspace workspace_of(uint8_t* out, int dtype, uint64_t n, uint64_t k) {
+  const uint64_t tiles = divup(n, 8192), blocks = divup(tiles, 64);
+  Workspace w;
+  uint64_t at = workspace_offset(dtype, n, k);
+  w.block_sum = reinterpret_cast<uint64_t*>(out + at);
+  at = round256(at + 8 * blocks);
+  w.tile_count = reinterpret_cast<uint32_t*>(out + at);  // 16-byte loads in encode_sums
+  at = round256(at + 4 * tiles);
+  w.stage = reinterpret_cast<uint32_t*>(out + at);
+  at += 4 * 512 * tiles;
+  w.end = round256(at);
+  return w;
 }
 
 // ----------------------------------------------------------------- helpers
@@ -148,8 +169,6 @@ __device__ inline uint32_t spread4(uint32_t w, int half) {
 struct PrepArgs {
   uint8_t* out;
   uint64_t n, seg_stored, nib, sm, esc, sm_bytes, offsets, chunks;
-  uint64_t* workspace;     // zeroed by prep_kernel
-  uint64_t workspace_words;
   uint64_t* out_bytes;
   uint32_t k, dtype, cb_first, cb_count, main;
   uint8_t cbs[kCbPerPrep * 16];
@@ -159,15 +178,13 @@ __device__ inline void put_le(uint8_t* p, uint64_t v, int bytes) {
   for (int i = 0; i < bytes; ++i) p[i] = (uint8_t)(v >> (8 * i));
 }
 
-// Header, codebooks, zero padding; clears the encoder's workspace.
+// Header, codebooks and zero padding.
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   const uint64_t gtid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
   const uint64_t gsize = (uint64_t)gridDim.x * kThreads;
   for (uint64_t i = gtid; i < (uint64_t)a.cb_count * 16; i += gsize)
     a.out[64 + 16 * (uint64_t)a.cb_first + i] = a.cbs[i];
-  if (!a.main) return;
-  for (uint64_t i = gtid; i < a.workspace_words; i += gsize) a.workspace[i] = 0;
-  if (blockIdx.x != 0) return;
+  if (!a.main || blockIdx.x != 0) return;
   const uint32_t t = threadIdx.x;
   // zero padding after the offsets, the nibbles and the sign|mantissa bytes
   const uint64_t ends[3] = {a.offsets + 8 * (a.chunks + 1), a.nib + divup(a.n, 2), a.sm + a.sm_bytes};
@@ -197,63 +214,62 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 
 // ---------------------------------------------------------- encode kernels
 //
-// One cooperative launch of G co-resident workgroups.  Tiles are dealt
-// round-robin: in round k workgroup b encodes tile kG + b, so the tiles in
-// flight at any moment are neighbours in memory.
-//   pass 1    for each of its tiles: dense encode (codes, sign|mantissa),
-//             element-order escape ranks; the tile's escape count goes to the
-//             workspace and its escape records are staged in LDS while they
-//             fit.
-//   pass 1.5  workgroup b scans the counts of rounds b, b + G, ...: escape
-//             offset of each tile inside its round, and the round's total.
-//   pass 2    every workgroup walks the rounds in order keeping the running
-//             total of earlier rounds, so each of its tiles knows its global
-//             escape offset; staged records are written there, chunk offsets
-//             and (for the last tile) E and S too.  Tiles whose escapes did
-//             not fit the stage are read again and written directly.
-// Counts, offsets and totals cross workgroups as flagged words; a reader
-// waits only for words whose producer is resident (cooperative launch) and
-// reaches them without waiting itself: pass 1 waits on nothing, pass 1.5 on
-// pass 1 words, pass 2 on pass 1 and 1.5 words.  So every wait ends.
+// Three launches after prep_kernel; no workgroup waits on another, so no
+// launch needs co-residency:
+//   encode_dense  one workgroup per 8192-element tile: dense encode (codes,
+//                 sign|mantissa) and element-order escape ranks.  The tile's
+//                 escape count goes to the workspace; when it holds at most
+//                 kStageSlot escapes its records go to the tile's staging
+//                 slot.
+//   encode_sums   one thread per block of kBlockTiles tiles: the block's
+//                 escape count.
+//   encode_place  one workgroup per block: block base = sum of the lower
+//                 blocks, scan of its tiles' counts, chunk offsets (E and S
+//                 for the last block), staged records copied to their place;
+//                 a tile whose escapes overflowed its slot is read again and
+//                 its records written directly.
 struct EncArgs {
   const uint8_t* in;
   uint8_t* out;
-  uint64_t n, n_tiles, offsets, nib, sm, esc, chunks;
-  uint64_t seg_chunks;     // chunks per codebook segment, 0 when one codebook
-  uint32_t* tile_count;    // per tile: escapes in it
-  uint32_t* tile_prefix;   // per tile: escapes before it in its round
-  uint64_t* round_sum;     // per round: escapes in it
+  uint64_t n, n_tiles, n_blocks, offsets, nib, sm, esc, chunks;
+  uint64_t seg_chunks;    // chunks per codebook segment, 0 when one codebook
+  uint32_t* tile_count;   // per tile: escapes in it
+  uint32_t* stage;        // per tile: kStageSlot records (position | exponent << 16)
+  uint64_t* block_sum;    // per block of kBlockTiles tiles: escapes in it
   uint64_t* out_bytes;
 };
 
-constexpr uint32_t kStage = 8192;  // escape records staged in LDS per workgroup
+constexpr uint32_t kStageSlot = 512;  // staged escape records per tile
 
-constexpr uint32_t kPerThread = 8;  // pass 1.5 handles rounds of up to 2048 tiles
+constexpr uint32_t kBlockTiles = 64;  // tiles per encode_place workgroup
 
 struct EncShared {
-  uint16_t st_pos[kStage];
-  uint8_t st_val[kStage];
   uint8_t table[256];
   uint32_t wave[8];
-  uint64_t red[4];
-  uint64_t p2_base[kThreads];
-  uint32_t p2_cnt[kThreads];
-  uint32_t p2_at[kThreads];
+  uint64_t red[16];
+};
+
+struct PlaceShared {
+  uint64_t red[16];
+  uint32_t pre_all[kBlockTiles + 1];     // escapes before each tile of the block
+  uint32_t pre_staged[kBlockTiles + 1];  // staged records before each tile of the block
+  uint32_t overflow;                     // some tile of the block is not staged
 };
 
 // Exclusive prefix over the workgroup's threads (thread order) of per-thread
-// u32 values whose sum over any wave fits 32 bits; *total gets the sum.
-__device__ inline uint64_t block_exclusive_sum(EncShared& sh, uint32_t v, uint64_t* total) {
+// u32 values whose sum over the workgroup fits 32 bits; *total gets the sum.
+template <int kWaves>
+__device__ inline uint32_t block_exclusive_sum(uint64_t* red, uint32_t v, uint32_t* total) {
   const uint32_t inc = wave_inclusive_sum(v);
   const uint32_t wave = threadIdx.x >> 6;
-  __syncthreads();  // earlier readers of sh.red are done
-  if ((threadIdx.x & 63) == 63) sh.red[wave] = inc;
+  __syncthreads();  // earlier readers of red are done
+  if ((threadIdx.x & 63) == 63) red[wave] = inc;
   __syncthreads();
-  uint64_t pre = 0, tot = 0;
+  uint32_t pre = 0, tot = 0;
 #pragma unroll
-  for (uint32_t w = 0; w < 4; ++w) {
-    pre += w < wave ? sh.red[w] : 0u;
-    tot += sh.red[w];
+  for (uint32_t w = 0; w < kWaves; ++w) {
+    pre += w < wave ? (uint32_t)red[w] : 0u;
+    tot += (uint32_t)red[w];
   }
   *total = tot;
   return pre + inc - v;
@@ -286,21 +302,30 @@ __device__ inline void wave_totals_to_lds(EncShared& sh, uint32_t i01, uint32_t 
 
 // BF16 tile: 8192 elements = 4 groups of 2048; thread t owns elements
 // 8t..8t+7 of each group (16-byte loads, coalesced per wave).
-__device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t tile, bool store) {
+// Input of one BF16 tile in registers (loaded ahead of its encode).
+struct TileIn {
+  uint4 w[4];
+};
+
+__device__ inline uint32_t valid_in_group(uint64_t n, uint64_t e0, uint32_t width) {
+  return e0 >= n ? 0u : (uint32_t)std::min<uint64_t>(width, n - e0);
+}
+
+__device__ inline TileIn load_tile_bf16(const EncArgs& a, uint64_t tile) {
   const uint32_t tid = threadIdx.x;
   const uint64_t first = tile * kEncTile;
   const uint16_t* in16 = reinterpret_cast<const uint16_t*>(a.in);
-  uint4 w[4];
-  uint32_t valid[4];
+  TileIn in;
+  uint4* w = in.w;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const uint64_t e0 = first + g * 2048 + 8 * tid;
-    valid[g] = e0 >= a.n ? 0u : (uint32_t)std::min<uint64_t>(8, a.n - e0);
-    if (valid[g] == 8) {
+    const uint32_t valid = valid_in_group(a.n, e0, 8);
+    if (valid == 8) {
       w[g] = *reinterpret_cast<const uint4*>(in16 + e0);
     } else {
       uint32_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
-      for (uint32_t j = 0; j < valid[g]; ++j) {
+      for (uint32_t j = 0; j < valid; ++j) {
         const uint32_t x = (uint32_t)in16[e0 + j] << (16 * (j & 1));
         if (j < 2) v0 |= x;
         else if (j < 4) v1 |= x;
@@ -310,6 +335,16 @@ __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t ti
       w[g] = make_uint4(v0, v1, v2, v3);
     }
   }
+  return in;
+}
+
+__device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store) {
+  const uint32_t tid = threadIdx.x;
+  const uint64_t first = tile * kEncTile;
+  const uint4* w = in.w;
+  uint32_t valid[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) valid[g] = valid_in_group(a.n, first + g * 2048 + 8 * tid, 8);
   TileEsc r;
   uint32_t cnt[4];
 #pragma unroll
@@ -395,11 +430,11 @@ __device__ inline uint32_t signmant12(uint32_t w) {
   return (v & 0x3Fu) | ((v >> 10) & 0xFC0u);
 }
 
-__device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t tile, bool store) {
-  const uint32_t tid = threadIdx.x;
-  const uint64_t e0 = tile * kEncTile + 32 * tid;
-  const uint32_t valid = e0 >= a.n ? 0u : (uint32_t)std::min<uint64_t>(32, a.n - e0);
-  uint32_t w[8];
+__device__ inline TileIn load_tile_e5m2(const EncArgs& a, uint64_t tile) {
+  const uint64_t e0 = tile * kEncTile + 32 * threadIdx.x;
+  const uint32_t valid = valid_in_group(a.n, e0, 32);
+  TileIn in;
+  uint32_t* w = reinterpret_cast<uint32_t*>(in.w);
   if (valid == 32) {
     const uint4 v0 = *reinterpret_cast<const uint4*>(a.in + e0);
     const uint4 v1 = *reinterpret_cast<const uint4*>(a.in + e0 + 16);
@@ -412,6 +447,13 @@ __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t ti
       for (uint32_t b = 0; b < 4 && 4 * k + b < valid; ++b) w[k] |= (uint32_t)a.in[e0 + 4 * k + b] << (8 * b);
     }
   }
+  return in;
+}
+
+__device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store) {
+  const uint64_t e0 = tile * kEncTile + 32 * threadIdx.x;
+  const uint32_t valid = valid_in_group(a.n, e0, 32);
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(in.w);
   uint32_t codes[8];
   TileEsc r;
   r.mask[0] = 0;
@@ -451,7 +493,7 @@ __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t ti
   }
   const uint32_t inc = wave_inclusive_sum(cnt);
   wave_totals_to_lds(sh, inc, 0);
-  const uint32_t wave = tid >> 6;
+  const uint32_t wave = threadIdx.x >> 6;
   uint32_t pre = 0, agg = 0;
 #pragma unroll
   for (uint32_t v = 0; v < 4; ++v) {
@@ -485,168 +527,148 @@ __device__ inline void put_record(const EncArgs& a, uint64_t index, uint32_t pos
   d[2] = (uint8_t)val;
 }
 
-// Cross-workgroup words carry a valid flag in the same atomic word, so a
-// relaxed agent-scope load that sees the flag also sees the value: no fence
-// (on this GPU an agent-scope fence writes back or invalidates the XCD's L2).
-constexpr uint32_t kValid32 = 1u << 31;
-constexpr uint64_t kValid64 = 1ull << 63;
+template <bool kBf16>
+__device__ void encode_dense(const EncArgs& a) {
+  __shared__ EncShared sh;
+  const uint64_t t = blockIdx.x;
+  build_table(a, sh, a.seg_chunks ? (t >> 3) / a.seg_chunks : 0, kBf16 ? 256u : 32u);
+  const TileIn in = kBf16 ? load_tile_bf16(a, t) : load_tile_e5m2(a, t);
+  const TileEsc r = kBf16 ? encode_tile_bf16(a, sh, t, in, true) : encode_tile_e5m2(a, sh, t, in, true);
+  if (threadIdx.x == 0) a.tile_count[t] = r.agg;
+  if (r.agg <= kStageSlot) {
+    uint32_t* slot = a.stage + t * kStageSlot;
+    auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) { slot[k] = pos | (val << 16); };
+    if (kBf16) for_each_escape_bf16(a, t, r, stage);
+    else for_each_escape_e5m2(a, t, r, stage);
+  }
+}
 
-__device__ inline void publish32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v | kValid32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__global__ __launch_bounds__(kThreads) void encode_dense_bf16_kernel(EncArgs a) { encode_dense<true>(a); }
+__global__ __launch_bounds__(kThreads) void encode_dense_e5m2_kernel(EncArgs a) { encode_dense<false>(a); }
+
+__global__ __launch_bounds__(kThreads) void encode_sums_kernel(EncArgs a) {
+  const uint64_t blk = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (blk >= a.n_blocks) return;
+  const uint64_t t0 = blk * kBlockTiles, t1 = std::min<uint64_t>(t0 + kBlockTiles, a.n_tiles);
+  uint64_t sum = 0;
+  if (t1 - t0 == kBlockTiles) {  // 16 x 16-byte loads, issued together
+    const uint4* c = reinterpret_cast<const uint4*>(a.tile_count + t0);
+    uint4 v[kBlockTiles / 4];
+#pragma unroll
+    for (uint32_t i = 0; i < kBlockTiles / 4; ++i) v[i] = c[i];
+#pragma unroll
+    for (uint32_t i = 0; i < kBlockTiles / 4; ++i) sum += (uint64_t)v[i].x + v[i].y + v[i].z + v[i].w;
+  } else {
+    for (uint64_t t = t0; t < t1; ++t) sum += a.tile_count[t];
+  }
+  a.block_sum[blk] = sum;
 }
-__device__ inline void publish64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v | kValid64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint32_t peek32(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint64_t peek64(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait for a published word; the caller's workgroup is resident and so is
-// its producer, which publishes without waiting on anything this one holds.
-__device__ inline uint32_t await32(const uint32_t* p) {
-  uint32_t v;
-  while (!((v = peek32(p)) & kValid32)) __builtin_amdgcn_s_sleep(4);
-  return v & ~kValid32;
-}
-__device__ inline uint64_t await64(const uint64_t* p) {
-  uint64_t v;
-  while (!((v = peek64(p)) & kValid64)) __builtin_amdgcn_s_sleep(4);
-  return v & ~kValid64;
-}
+
+constexpr uint32_t kPlaceBatch = 8;  // staged records per thread and step (loads issued together)
 
 template <bool kBf16>
-__device__ void encode_rounds(const EncArgs& a) {
-  __shared__ EncShared sh;
+__device__ void encode_place(const EncArgs& a) {
+  __shared__ PlaceShared sh;
+  __shared__ EncShared esh;
   const uint32_t tid = threadIdx.x;
-  const uint64_t G = gridDim.x, b = blockIdx.x;
-  const uint64_t rounds = divup(a.n_tiles, G);
-  const uint32_t entries = kBf16 ? 256u : 32u;
-  uint64_t table_cb = ~0ull;
-  uint32_t staged = 0;        // records in the LDS stage (same value in every thread)
-  uint64_t spill = rounds;    // first round whose records are not staged
+  const uint64_t blk = blockIdx.x;
+  // block base: escapes of all lower blocks
+  uint64_t part = 0;
+  for (uint64_t i = tid; i < blk; i += kThreads) part += a.block_sum[i];
+  {
+    // wave sum of u64 through two u32 halves; one lane per wave stores it
+    uint64_t v = part;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
+      const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
+      v += ((uint64_t)hi << 32) | lo;
+    }
+    if ((tid & 63) == 0) sh.red[8 + (tid >> 6)] = v;
+  }
+  __syncthreads();
+  const uint64_t base = sh.red[8] + sh.red[9] + sh.red[10] + sh.red[11];
 
-  // ---- pass 1
-  for (uint64_t k = 0; k < rounds; ++k) {
-    const uint64_t t = k * G + b;
-    if (t >= a.n_tiles) break;
-    const uint64_t cbi = a.seg_chunks ? (t >> 3) / a.seg_chunks : 0;
+  // this block's tiles (one per thread of the first wave): counts, in-block
+  // offsets, chunk offsets
+  const uint64_t t = blk * kBlockTiles + tid;
+  const bool mine = tid < kBlockTiles && t < a.n_tiles;
+  const uint32_t cnt = mine ? a.tile_count[t] : 0u;
+  const bool staged = cnt <= kStageSlot;
+  uint32_t total, staged_total;
+  const uint32_t pre = block_exclusive_sum<kThreads / 64>(sh.red, cnt, &total);
+  const uint32_t spre = block_exclusive_sum<kThreads / 64>(sh.red, staged ? cnt : 0u, &staged_total);
+  if (tid <= kBlockTiles) {
+    sh.pre_all[tid] = pre;
+    sh.pre_staged[tid] = spre;
+  }
+  if (tid == 0) sh.overflow = 0;
+  __syncthreads();
+  if (mine) {
+    if ((t & 7) == 0) put_le(a.out + a.offsets + 8 * (t >> 3), base + pre, 8);
+    if (!staged) atomicOr(&sh.overflow, 1u);
+    if (t == a.n_tiles - 1) {
+      const uint64_t e = std::min<uint64_t>(base + pre + cnt, a.n);
+      const uint64_t s = a.esc + 3 * e;
+      put_le(a.out + a.offsets + 8 * a.chunks, e, 8);
+      put_le(a.out + 16, e, 8);
+      put_le(a.out + 24, s, 8);
+      if (a.out_bytes) *a.out_bytes = s;
+    }
+  }
+  __syncthreads();
+
+  // staged records of the block, flattened: record j belongs to the tile i
+  // with pre_staged[i] <= j < pre_staged[i + 1]
+  const uint32_t tiles = (uint32_t)std::min<uint64_t>(kBlockTiles, a.n_tiles - blk * kBlockTiles);
+  for (uint32_t j0 = 0; j0 < staged_total; j0 += kThreads * kPlaceBatch) {
+    uint32_t v[kPlaceBatch];
+    uint64_t dst[kPlaceBatch];
+#pragma unroll
+    for (uint32_t u = 0; u < kPlaceBatch; ++u) {
+      const uint32_t j = j0 + u * kThreads + tid;
+      dst[u] = ~0ull;
+      if (j < staged_total) {
+        uint32_t lo = 0, hi = tiles;  // last i with pre_staged[i] <= j
+        while (hi - lo > 1) {
+          const uint32_t mid = (lo + hi) >> 1;
+          if (sh.pre_staged[mid] <= j) lo = mid;
+          else hi = mid;
+        }
+        const uint32_t r = j - sh.pre_staged[lo];
+        v[u] = a.stage[(blk * kBlockTiles + lo) * kStageSlot + r];
+        dst[u] = base + sh.pre_all[lo] + r;
+      }
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < kPlaceBatch; ++u)
+      if (dst[u] != ~0ull) put_record(a, dst[u], v[u] & 0xFFFF, v[u] >> 16);
+  }
+  if (!sh.overflow) return;  // uniform
+
+  // tiles whose escapes overflowed their slot: read them again
+  uint64_t table_cb = ~0ull;
+  for (uint32_t i = 0; i < tiles; ++i) {
+    const uint32_t n_i = sh.pre_all[i + 1] - sh.pre_all[i];
+    if (n_i <= kStageSlot) continue;  // uniform
+    const uint64_t tt = blk * kBlockTiles + i;
+    const uint64_t cbi = a.seg_chunks ? (tt >> 3) / a.seg_chunks : 0;
     if (cbi != table_cb) {
-      build_table(a, sh, cbi, entries);
+      build_table(a, esh, cbi, kBf16 ? 256u : 32u);
       table_cb = cbi;
     }
-    const TileEsc r = kBf16 ? encode_tile_bf16(a, sh, t, true) : encode_tile_e5m2(a, sh, t, true);
-    if (tid == 0) publish32(&a.tile_count[t], r.agg);
-    if (spill == rounds && staged + r.agg <= kStage) {
-      const uint32_t at = staged;
-      auto stage = [&](uint32_t i, uint32_t pos, uint32_t val) {
-        sh.st_pos[at + i] = (uint16_t)pos;
-        sh.st_val[at + i] = (uint8_t)val;
-      };
-      if (kBf16) for_each_escape_bf16(a, t, r, stage);
-      else for_each_escape_e5m2(a, t, r, stage);
-      staged += r.agg;
-    } else if (spill == rounds) {
-      spill = k;
-    }
-    __syncthreads();  // the wave totals in LDS are reused by the next tile
-  }
-
-  // ---- pass 1.5: scan of the counts of rounds b, b + G, ...; thread i
-  // takes a run of consecutive tiles of the round, all loads issued at once
-  const uint32_t per = (uint32_t)divup(G, kThreads);  // tiles per thread (<= kPerThread)
-  for (uint64_t k = b; k < rounds; k += G) {
-    const uint64_t t0 = k * G + (uint64_t)tid * per, t1 = std::min<uint64_t>((k + 1) * G, a.n_tiles);
-    uint32_t c[kPerThread];
-    uint32_t mine = 0;
-#pragma unroll
-    for (uint32_t j = 0; j < kPerThread; ++j)  // issue every load, then wait for stragglers
-      c[j] = (j < per && t0 + j < t1) ? peek32(&a.tile_count[t0 + j]) : kValid32;
-#pragma unroll
-    for (uint32_t j = 0; j < kPerThread; ++j) {
-      if (!(c[j] & kValid32)) c[j] = await32(&a.tile_count[t0 + j]);
-      c[j] &= ~kValid32;
-      mine += c[j];
-    }
-    uint64_t total;
-    uint32_t run = (uint32_t)block_exclusive_sum(sh, mine, &total);
-#pragma unroll
-    for (uint32_t j = 0; j < kPerThread; ++j) {
-      if (j < per && t0 + j < t1) publish32(&a.tile_prefix[t0 + j], run);
-      run += c[j];
-    }
-    if (tid == 0) publish64(&a.round_sum[k], total);
-  }
-
-  // ---- pass 2, 256 rounds at a time: thread i loads round k0 + i's total
-  // and this workgroup's tile of that round; block scans give every tile its
-  // global escape offset and its place in the LDS stage.
-  uint64_t before = 0;  // escapes in rounds before k0
-  uint32_t at = 0;      // staged records of tiles before round k0
-  for (uint64_t k0 = 0; k0 < rounds; k0 += kThreads) {
-    const uint64_t k = k0 + tid;
-    const uint64_t t = k * G + b;
-    uint32_t rsum = 0, cnt = 0, tpre = 0;
-    if (k < rounds) {
-      uint64_t r64 = peek64(&a.round_sum[k]);
-      if (t < a.n_tiles) {
-        cnt = peek32(&a.tile_count[t]);
-        tpre = peek32(&a.tile_prefix[t]);
-        cnt = (cnt & kValid32) ? cnt & ~kValid32 : await32(&a.tile_count[t]);
-        tpre = (tpre & kValid32) ? tpre & ~kValid32 : await32(&a.tile_prefix[t]);
-      }
-      rsum = (uint32_t)((r64 & kValid64) ? r64 & ~kValid64 : await64(&a.round_sum[k]));
-    }
-    uint64_t rtotal, ctotal;
-    const uint64_t rpre = block_exclusive_sum(sh, rsum, &rtotal);
-    const uint64_t cpre = block_exclusive_sum(sh, k < spill ? cnt : 0u, &ctotal);
-    const uint64_t base = before + rpre + tpre;
-    if (k < rounds && t < a.n_tiles) {
-      if ((t & 7) == 0) put_le(a.out + a.offsets + 8 * (t >> 3), base, 8);
-      if (t == a.n_tiles - 1) {
-        const uint64_t e = std::min<uint64_t>(base + cnt, a.n);
-        const uint64_t s = a.esc + 3 * e;
-        put_le(a.out + a.offsets + 8 * a.chunks, e, 8);
-        put_le(a.out + 16, e, 8);
-        put_le(a.out + 24, s, 8);
-        if (a.out_bytes) *a.out_bytes = s;
-      }
-    }
-    sh.p2_base[tid] = base;
-    sh.p2_cnt[tid] = cnt;
-    sh.p2_at[tid] = at + (uint32_t)cpre;
-    __syncthreads();
-    const uint32_t batch = (uint32_t)std::min<uint64_t>(kThreads, rounds - k0);
-    for (uint32_t i = 0; i < batch; ++i) {
-      const uint64_t kk = k0 + i, tt = kk * G + b;
-      if (tt >= a.n_tiles) break;
-      const uint64_t tb = sh.p2_base[i];
-      if (kk < spill) {
-        const uint32_t n_i = sh.p2_cnt[i], a_i = sh.p2_at[i];
-        for (uint32_t r = tid; r < n_i; r += kThreads) put_record(a, tb + r, sh.st_pos[a_i + r], sh.st_val[a_i + r]);
-      } else {
-        // not staged: read the tile again and write its records directly
-        const uint64_t cbi = a.seg_chunks ? (tt >> 3) / a.seg_chunks : 0;
-        if (cbi != table_cb) {
-          build_table(a, sh, cbi, entries);
-          table_cb = cbi;
-        }
-        const TileEsc r = kBf16 ? encode_tile_bf16(a, sh, tt, false) : encode_tile_e5m2(a, sh, tt, false);
-        auto direct = [&](uint32_t j, uint32_t pos, uint32_t val) { put_record(a, tb + j, pos, val); };
-        if (kBf16) for_each_escape_bf16(a, tt, r, direct);
-        else for_each_escape_e5m2(a, tt, r, direct);
-        __syncthreads();
-      }
-    }
-    before += rtotal;
-    at += (uint32_t)ctotal;
-    __syncthreads();
+    const TileIn in = kBf16 ? load_tile_bf16(a, tt) : load_tile_e5m2(a, tt);
+    const TileEsc r = kBf16 ? encode_tile_bf16(a, esh, tt, in, false) : encode_tile_e5m2(a, esh, tt, in, false);
+    const uint64_t at = base + sh.pre_all[i];
+    auto direct = [&](uint32_t k, uint32_t pos, uint32_t val) { put_record(a, at + k, pos, val); };
+    if (kBf16) for_each_escape_bf16(a, tt, r, direct);
+    else for_each_escape_e5m2(a, tt, r, direct);
+    __syncthreads();  // esh is reused by the next tile
   }
 }
 
-__global__ __launch_bounds__(kThreads) void encode_bf16_kernel(EncArgs a) { encode_rounds<true>(a); }
-__global__ __launch_bounds__(kThreads) void encode_e5m2_kernel(EncArgs a) { encode_rounds<false>(a); }
+__global__ __launch_bounds__(kThreads) void encode_place_bf16_kernel(EncArgs a) { encode_place<true>(a); }
+__global__ __launch_bounds__(kThreads) void encode_place_e5m2_kernel(EncArgs a) { encode_place<false>(a); }
 
 // ---------------------------------------------------------- decode kernels
 struct DecArgs {
@@ -775,16 +797,27 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
   const uint64_t chunk = tile / (kChunk / kDecTile);
   const uint64_t cbi = h.k == 1 ? 0 : (chunk * kChunk) / h.seg;
   const uint8_t* cb = a.in + 64 + 16 * cbi;
+  const uint32_t tid = threadIdx.x;
+  const uint64_t first = tile * kDecTile;
+  // issue the tile's dense loads first: the escape staging overlaps them
+  uint32_t nibs[8];
+  uint2 sms[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const uint64_t e0 = first + g * 2048 + 8 * tid;
+    if (e0 + 8 <= a.n) {
+      nibs[g] = ld32(a.in + h.s.nib + e0 / 2);
+      sms[g] = *reinterpret_cast<const uint2*>(a.in + h.s.sm + e0);
+    }
+  }
   const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4), l2 = ld32(cb + 8), l3 = ld32(cb + 12);
   if (!stage_escapes(a, h, tile, bitmap, vals, s_range, &s_err)) {
     if (threadIdx.x == 0) report_corrupt(a.status);
     return;
   }
-  const uint32_t tid = threadIdx.x;
-  const uint64_t first = tile * kDecTile;
   const uint8_t* bm8 = reinterpret_cast<const uint8_t*>(bitmap);
   uint16_t* out16 = reinterpret_cast<uint16_t*>(a.out);
-  #pragma unroll 2
+#pragma unroll
   for (int g = 0; g < 8; ++g) {
     const uint32_t local = g * 2048 + 8 * tid;
     const uint64_t e0 = first + local;
@@ -793,8 +826,8 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
     uint32_t nib;
     uint2 sm;
     if (valid == 8) {
-      nib = ld32(a.in + h.s.nib + e0 / 2);
-      sm = *reinterpret_cast<const uint2*>(a.in + h.s.sm + e0);
+      nib = nibs[g];
+      sm = sms[g];
     } else {
       uint32_t tn = 0, t0 = 0, t1 = 0;
       for (uint32_t b = 0; b < (valid + 1) / 2; ++b) tn |= (uint32_t)a.in[h.s.nib + e0 / 2 + b] << (8 * b);
@@ -854,6 +887,22 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
   const uint64_t chunk = tile / (kChunk / kDecTile);
   const uint64_t cbi = h.k == 1 ? 0 : (chunk * kChunk) / h.seg;
   const uint8_t* cb = a.in + 64 + 16 * cbi;
+  const uint32_t tid = threadIdx.x;
+  const uint64_t first = tile * kDecTile;
+  // issue the tile's dense loads first: the escape staging overlaps them
+  uint4 pn[2];
+  uint32_t ps[2][3];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const uint64_t e0 = first + g * 8192 + 32 * tid;
+    if (e0 + 32 <= a.n) {
+      const uint64_t smo = h.s.sm + 3 * (e0 / 8);
+      pn[g] = *reinterpret_cast<const uint4*>(a.in + h.s.nib + e0 / 2);
+      ps[g][0] = ld32(a.in + smo);
+      ps[g][1] = ld32(a.in + smo + 4);
+      ps[g][2] = ld32(a.in + smo + 8);
+    }
+  }
   const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4), l2 = ld32(cb + 8), l3 = ld32(cb + 12);
   if (((l0 | l1 | l2 | l3) & 0xE0E0E0E0u) != 0) {  // E5M2 exponents are 5 bits
     if (threadIdx.x == 0) report_corrupt(a.status);
@@ -863,9 +912,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
     if (threadIdx.x == 0) report_corrupt(a.status);
     return;
   }
-  const uint32_t tid = threadIdx.x;
-  const uint64_t first = tile * kDecTile;
-  #pragma unroll 1
+#pragma unroll
   for (int g = 0; g < 2; ++g) {
     const uint32_t local = g * 8192 + 32 * tid;
     const uint64_t e0 = first + local;
@@ -874,11 +921,10 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
     uint32_t nib[4], sw[3];
     const uint64_t smo = h.s.sm + 3 * (e0 / 8);
     if (valid == 32) {
-      const uint4 v = *reinterpret_cast<const uint4*>(a.in + h.s.nib + e0 / 2);
-      nib[0] = v.x; nib[1] = v.y; nib[2] = v.z; nib[3] = v.w;
-      sw[0] = ld32(a.in + smo);
-      sw[1] = ld32(a.in + smo + 4);
-      sw[2] = ld32(a.in + smo + 8);
+      nib[0] = pn[g].x; nib[1] = pn[g].y; nib[2] = pn[g].z; nib[3] = pn[g].w;
+      sw[0] = ps[g][0];
+      sw[1] = ps[g][1];
+      sw[2] = ps[g][2];
     } else {
       const uint32_t nb = (valid + 1) / 2, sb = 3 * ((valid + 7) / 8);
       #pragma unroll
@@ -924,7 +970,6 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
   }
 }
 
-__global__ void set_status_kernel(int32_t* status) { *status = SPLITZIP_OK; }
 
 // ------------------------------------------------------------ host helpers
 bool dtype_valid(int dtype) { return dtype == SPLITZIP_BF16 || dtype == SPLITZIP_FP8_E5M2; }
@@ -969,7 +1014,7 @@ int splitzip_calibrate(int dtype, const void* host_samples, size_t n_elems, uint
 
 size_t splitzip_max_compressed_size(int dtype, size_t n_elems, uint32_t n_codebooks) {
   if (!dtype_valid(dtype) || n_codebooks == 0 || n_codebooks > kMaxK || n_elems > kMaxN) return 0;
-  return workspace_offset(dtype, n_elems, n_codebooks) + 16 * divup(n_elems, kEncTile);
+  return workspace_of(nullptr, dtype, n_elems, n_codebooks).end;
 }
 
 int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks, uint32_t n_codebooks,
@@ -989,10 +1034,7 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
   const Sections s = sections_of(dtype, n, n_codebooks);
   const uint64_t n_tiles = divup(n, kEncTile);
   uint8_t* out = static_cast<uint8_t*>(d_out);
-  const uint64_t ws = workspace_offset(dtype, n, n_codebooks);
-  uint64_t* round_sum = reinterpret_cast<uint64_t*>(out + ws);  // at most n_tiles rounds
-  uint32_t* tile_count = reinterpret_cast<uint32_t*>(round_sum + n_tiles);
-  uint32_t* tile_prefix = tile_count + n_tiles;
+  const Workspace w = workspace_of(out, dtype, n, n_codebooks);
 
   for (uint32_t first = 0; first < n_codebooks; first += kCbPerPrep) {
     PrepArgs p;
@@ -1006,8 +1048,6 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
     p.sm_bytes = s.sm_bytes;
     p.offsets = s.offsets;
     p.chunks = s.chunks;
-    p.workspace = round_sum;
-    p.workspace_words = 2 * n_tiles;
     p.out_bytes = d_out_bytes;
     p.k = n_codebooks;
     p.dtype = (uint32_t)dtype;
@@ -1015,8 +1055,7 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
     p.cb_count = std::min<uint32_t>(kCbPerPrep, n_codebooks - first);
     p.main = first == 0;
     memcpy(p.cbs, h_codebooks + 16ull * first, 16ull * p.cb_count);
-    const uint64_t work = std::max<uint64_t>(p.main ? divup(p.workspace_words, 4) : 0, 16ull * p.cb_count);
-    const uint32_t blocks = (uint32_t)std::min<uint64_t>(2048, std::max<uint64_t>(1, divup(work, kThreads)));
+    const uint32_t blocks = (uint32_t)std::max<uint64_t>(1, divup(16ull * p.cb_count, kThreads));
     prep_kernel<<<blocks, kThreads, 0, stream>>>(p);
     if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
   }
@@ -1033,25 +1072,21 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
   e.esc = s.esc;
   e.chunks = s.chunks;
   e.seg_chunks = n_codebooks == 1 ? 0 : segment_elems / kChunk;
-  e.tile_count = tile_count;
-  e.tile_prefix = tile_prefix;
-  e.round_sum = round_sum;
+  e.tile_count = w.tile_count;
+  e.stage = w.stage;
+  e.block_sum = w.block_sum;
   e.out_bytes = d_out_bytes;
-  const void* kernel = dtype == SPLITZIP_BF16 ? reinterpret_cast<const void*>(&encode_bf16_kernel)
-                                              : reinterpret_cast<const void*>(&encode_e5m2_kernel);
-  // the waits need every workgroup resident: a cooperative launch of at most
-  // the number of co-resident workgroups, and at most one per tile
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || cus <= 0 ||
-      per_cu <= 0)
-    return SPLITZIP_E_HIP;
-  const uint32_t grid = (uint32_t)std::min<uint64_t>(
-      std::min<uint64_t>(n_tiles, (uint64_t)cus * (uint64_t)per_cu), (uint64_t)kThreads * kPerThread);
-  void* args[] = {&e};
-  if (hipLaunchCooperativeKernel(kernel, dim3(grid), dim3(kThreads), args, 0, stream) != hipSuccess)
-    return SPLITZIP_E_HIP;
+  const uint32_t tiles = (uint32_t)n_tiles;  // n <= 2^40 -> at most 2^27 tiles
+  const uint64_t blocks = divup(n_tiles, kBlockTiles);
+  e.n_blocks = blocks;
+  if (dtype == SPLITZIP_BF16) encode_dense_bf16_kernel<<<tiles, kThreads, 0, stream>>>(e);
+  else encode_dense_e5m2_kernel<<<tiles, kThreads, 0, stream>>>(e);
+  if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
+  encode_sums_kernel<<<(uint32_t)divup(blocks, kThreads), kThreads, 0, stream>>>(e);
+  if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
+  if (dtype == SPLITZIP_BF16) encode_place_bf16_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(e);
+  else encode_place_e5m2_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(e);
+  if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
   return SPLITZIP_OK;
 }
 
@@ -1060,10 +1095,6 @@ int splitzip_decompress(const void* d_in, size_t in_bytes, int dtype, size_t n_e
   if (!dtype_valid(dtype) || n_elems > kMaxN || d_in == nullptr || in_bytes < 64 || !aligned(d_in, 16) ||
       (d_out == nullptr && n_elems > 0) || !aligned(d_out, 16) || !aligned(d_status, 4))
     return SPLITZIP_E_INVALID;
-  if (d_status) {
-    set_status_kernel<<<1, 1, 0, stream>>>(d_status);
-    if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
-  }
   DecArgs a;
   a.in = static_cast<const uint8_t*>(d_in);
   a.in_bytes = in_bytes;

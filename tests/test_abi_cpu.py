@@ -51,7 +51,7 @@ def test_max_compressed_size():
     for dtype in (O.BF16, O.E5M2):
         for n, k in [(0, 1), (1, 1), (65537, 2), (536870912, 32)]:
             cap = sz.splitzip_max_compressed_size(dtype, n, k)
-            assert cap >= O.max_size(dtype, n, k) + 16 * (-(-n // 8192))
+            assert cap >= O.max_size(dtype, n, k) + 2052 * (-(-n // 8192))
             assert cap % 8 == 0
     assert sz.splitzip_max_compressed_size(3, 10, 1) == 0
     assert sz.splitzip_max_compressed_size(O.BF16, 10, 0) == 0

@@ -36,15 +36,14 @@ def test_full_size_workload(name):
     out, nb = sz.compress(wl.data, cbs, seg)
     torch.cuda.synchronize()
     n_bytes = int(nb.item())
+    gpu = out[:n_bytes].cpu().numpy()
+    xh = kvsynth.to_numpy_bits(wl.data)
+    E = compare_with_oracle(gpu, dtype, xh, cbs, seg)
     y, st = sz.decompress(out[:n_bytes], wl.n, dtype)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     assert torch.equal(y.view(torch.uint8), wl.data.view(torch.uint8))
-    del y
-    gpu = out[:n_bytes].cpu().numpy()
-    del out
-    xh = kvsynth.to_numpy_bits(wl.data)
-    E = compare_with_oracle(gpu, dtype, xh, cbs, seg)
+    del y, out
     eps = E / wl.n
     lo, hi = EXPECT[name]
     print(f"  n={wl.n} K={cbs.shape[0]} escapes={E} rate={eps:.5f} ratio={wl.raw_bytes / n_bytes:.4f}", flush=True)
