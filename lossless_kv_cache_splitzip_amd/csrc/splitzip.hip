@@ -95,6 +95,22 @@ __host__ inline Workspace workspace_of(uint8_t* out, int dtype, uint64_t n, uint
 }
 
 // ----------------------------------------------------------------- helpers
+// Streaming stores of the dense outputs: the codec never reads them back, so
+// they are written non-temporally.  Used where a wave's store instruction
+// covers contiguous memory (lane-contiguous words); for half-density
+// patterns non-temporal stores measured slower than plain ones.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline void store_stream(void* p, uint32_t v) { __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p)); }
+__device__ inline void store_stream(void* p, uint2 v) {
+  const u32x2_t t = {v.x, v.y};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ inline void store_stream(void* p, uint4 v) {
+  const u32x4_t t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+}
+
 __device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
@@ -247,6 +263,7 @@ struct EncShared {
   uint8_t table[256];
   uint32_t wave[8];
   uint64_t red[16];
+  alignas(16) uint32_t s3[4 * 96];  // E5M2: a wave's 64 x 6 sign|mantissa bytes, gathered for aligned stores
 };
 
 struct PlaceShared {
@@ -287,8 +304,8 @@ __device__ inline void build_table(const EncArgs& a, EncShared& sh, uint64_t cbi
 // thread's first escape in each group, and the escape masks.
 struct TileEsc {
   uint32_t agg;      // escapes in the tile
-  uint32_t rank[4];  // BF16: per group of 8; E5M2: rank[0] only
-  uint32_t mask[4];  // BF16: 8-bit masks per group; E5M2: mask[0] 32-bit
+  uint32_t rank[4];  // BF16: per group of 8 (4 groups); E5M2: per group of 16 (2 groups)
+  uint32_t mask[4];  // escaped elements of each group, bit j = element j
 };
 
 __device__ inline void wave_totals_to_lds(EncShared& sh, uint32_t i01, uint32_t i23) {
@@ -368,8 +385,8 @@ __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t ti
       const uint32_t sm1 = (h23 & 0x80808080u) | (l23 & 0x7F7F7F7Fu);
       const uint64_t e0 = first + g * 2048 + 8 * tid;
       if (valid[g] == 8) {
-        *reinterpret_cast<uint32_t*>(a.out + a.nib + e0 / 2) = nib;
-        *reinterpret_cast<uint2*>(a.out + a.sm + e0) = make_uint2(sm0, sm1);
+        store_stream(a.out + a.nib + e0 / 2, nib);
+        store_stream(a.out + a.sm + e0, make_uint2(sm0, sm1));
       } else if (valid[g] > 0) {
         for (uint32_t b = 0; b < (valid[g] + 1) / 2; ++b) a.out[a.nib + e0 / 2 + b] = (uint8_t)(nib >> (8 * b));
         for (uint32_t j = 0; j < valid[g]; ++j) a.out[a.sm + e0 + j] = (uint8_t)((j < 4 ? sm0 : sm1) >> (8 * (j & 3)));
@@ -421,8 +438,7 @@ __device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, con
   }
 }
 
-// E5M2: a thread owns 32 consecutive elements (32 input bytes, 16 nibble
-// bytes, 12 sign|mantissa bytes).
+// Four E5M2 bytes -> their 3-bit sign|mantissa values packed into 12 bits.
 __device__ inline uint32_t signmant12(uint32_t w) {
   // byte k -> 3-bit value sign<<2 | mantissa, then 4 x 3 bits -> 12 bits
   const uint32_t u = ((w >> 5) & 0x04040404u) | (w & 0x03030303u);
@@ -430,92 +446,112 @@ __device__ inline uint32_t signmant12(uint32_t w) {
   return (v & 0x3Fu) | ((v >> 10) & 0xFC0u);
 }
 
+// E5M2 tile: 8192 elements = 2 groups of 4096; thread t owns elements
+// 16t..16t+15 of each group: 16 input bytes, 8 nibble bytes and 6
+// sign|mantissa bytes, all lane-contiguous across a wave.
 __device__ inline TileIn load_tile_e5m2(const EncArgs& a, uint64_t tile) {
-  const uint64_t e0 = tile * kEncTile + 32 * threadIdx.x;
-  const uint32_t valid = valid_in_group(a.n, e0, 32);
   TileIn in;
-  uint32_t* w = reinterpret_cast<uint32_t*>(in.w);
-  if (valid == 32) {
-    const uint4 v0 = *reinterpret_cast<const uint4*>(a.in + e0);
-    const uint4 v1 = *reinterpret_cast<const uint4*>(a.in + e0 + 16);
-    w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
-    w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
-  } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      w[k] = 0;
-      for (uint32_t b = 0; b < 4 && 4 * k + b < valid; ++b) w[k] |= (uint32_t)a.in[e0 + 4 * k + b] << (8 * b);
+  for (int g = 0; g < 2; ++g) {
+    const uint64_t e0 = tile * kEncTile + g * 4096 + 16 * threadIdx.x;
+    const uint32_t valid = valid_in_group(a.n, e0, 16);
+    if (valid == 16) {
+      in.w[g] = *reinterpret_cast<const uint4*>(a.in + e0);
+    } else {
+      uint32_t v[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        for (uint32_t b = 0; b < 4 && 4 * k + b < valid; ++b) v[k] |= (uint32_t)a.in[e0 + 4 * k + b] << (8 * b);
+      in.w[g] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   }
   return in;
 }
 
 __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store) {
-  const uint64_t e0 = tile * kEncTile + 32 * threadIdx.x;
-  const uint32_t valid = valid_in_group(a.n, e0, 32);
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(in.w);
-  uint32_t codes[8];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool tile_full = (tile + 1) * kEncTile <= a.n;  // same in every thread
   TileEsc r;
-  r.mask[0] = 0;
+  uint32_t cnt[2];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t x = w[k];
-    const uint8_t* tb = sh.table;
-    uint32_t c = gather4(tb[(x >> 2) & 0x1F], tb[(x >> 10) & 0x1F], tb[(x >> 18) & 0x1F], tb[(x >> 26) & 0x1F]);
-    if (valid < 32) c &= keep_low_bytes(valid > 4u * k ? valid - 4u * k : 0u);
-    codes[k] = c;
-    r.mask[0] |= flag_mask4(c) << (4 * k);
-  }
-  const uint32_t cnt = __builtin_popcount(r.mask[0]);
-  if (store) {
-    uint32_t nib[4];
+  for (int g = 0; g < 2; ++g) {
+    const uint64_t e0 = tile * kEncTile + g * 4096 + 16 * tid;
+    const uint32_t valid = valid_in_group(a.n, e0, 16);
+    const uint32_t w[4] = {in.w[g].x, in.w[g].y, in.w[g].z, in.w[g].w};
+    uint32_t c[4];
+    r.mask[g] = 0;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) nib[d] = pack_nibbles(codes[2 * d], codes[2 * d + 1]);
-    uint32_t g24[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) g24[d] = signmant12(w[2 * d]) | (signmant12(w[2 * d + 1]) << 12);
-    const uint32_t s0 = g24[0] | (g24[1] << 24);
-    const uint32_t s1 = (g24[1] >> 8) | (g24[2] << 16);
-    const uint32_t s2 = (g24[2] >> 16) | (g24[3] << 8);
-    const uint64_t smo = a.sm + 3 * (e0 / 8);
-    if (valid == 32) {
-      *reinterpret_cast<uint4*>(a.out + a.nib + e0 / 2) = make_uint4(nib[0], nib[1], nib[2], nib[3]);
-      uint32_t* sp = reinterpret_cast<uint32_t*>(a.out + smo);
-      sp[0] = s0;
-      sp[1] = s1;
-      sp[2] = s2;
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t x = w[k];
+      const uint8_t* tb = sh.table;
+      c[k] = gather4(tb[(x >> 2) & 0x1F], tb[(x >> 10) & 0x1F], tb[(x >> 18) & 0x1F], tb[(x >> 26) & 0x1F]);
+      if (valid < 16) c[k] &= keep_low_bytes(valid > 4u * k ? valid - 4u * k : 0u);
+      r.mask[g] |= flag_mask4(c[k]) << (4 * k);
+    }
+    cnt[g] = __builtin_popcount(r.mask[g]);
+    if (!store) continue;
+    const uint2 nib = make_uint2(pack_nibbles(c[0], c[1]), pack_nibbles(c[2], c[3]));
+    // 16 triples = 48 bits, element i at bit 3i
+    const uint32_t s0 = signmant12(w[0]), s1 = signmant12(w[1]), s2 = signmant12(w[2]), s3 = signmant12(w[3]);
+    const uint32_t lo = s0 | (s1 << 12) | (s2 << 24);
+    const uint32_t hi = (s2 >> 8) | (s3 << 4);
+    const uint64_t smo = a.sm + 6 * (e0 / 16);
+    if (tile_full) {
+      store_stream(a.out + a.nib + e0 / 2, nib);
+      // gather the wave's 64 x 6 bytes in LDS, then 24 aligned 16-byte stores
+      uint8_t* buf = reinterpret_cast<uint8_t*>(sh.s3 + wave * 96);
+      if ((lane & 1) == 0) {
+        *reinterpret_cast<uint32_t*>(buf + 6 * lane) = lo;
+        *reinterpret_cast<uint16_t*>(buf + 6 * lane + 4) = (uint16_t)hi;
+      } else {
+        *reinterpret_cast<uint16_t*>(buf + 6 * lane) = (uint16_t)lo;
+        *reinterpret_cast<uint32_t*>(buf + 6 * lane + 2) = (lo >> 16) | (hi << 16);
+      }
+      __syncthreads();
+      if (lane < 24) {
+        const uint64_t wave_smo = a.sm + 6 * ((tile * kEncTile + g * 4096 + 1024 * wave) / 16);
+        store_stream(a.out + wave_smo + 16 * lane, *reinterpret_cast<const uint4*>(buf + 16 * lane));
+      }
+      __syncthreads();
     } else if (valid > 0) {
       for (uint32_t b = 0; b < (valid + 1) / 2; ++b)
-        a.out[a.nib + e0 / 2 + b] = (uint8_t)(pick4(nib[0], nib[1], nib[2], nib[3], b >> 2) >> (8 * (b & 3)));
+        a.out[a.nib + e0 / 2 + b] = (uint8_t)((b < 4 ? nib.x : nib.y) >> (8 * (b & 3)));
       for (uint32_t b = 0; b < 3 * ((valid + 7) / 8); ++b)
-        a.out[smo + b] = (uint8_t)(pick4(s0, s1, s2, 0u, b >> 2) >> (8 * (b & 3)));
+        a.out[smo + b] = (uint8_t)((b < 4 ? lo : hi) >> (8 * (b & 3)));
     }
   }
-  const uint32_t inc = wave_inclusive_sum(cnt);
+  // element-order ranks: groups are ordered (g, thread); two 16-bit fields
+  const uint32_t p = cnt[0] | (cnt[1] << 16);
+  const uint32_t inc = wave_inclusive_sum(p);
   wave_totals_to_lds(sh, inc, 0);
-  const uint32_t wave = threadIdx.x >> 6;
-  uint32_t pre = 0, agg = 0;
+  uint32_t pre = 0, tot = 0;
 #pragma unroll
   for (uint32_t v = 0; v < 4; ++v) {
     pre += v < wave ? sh.wave[v] : 0u;
-    agg += sh.wave[v];
+    tot += sh.wave[v];
   }
-  r.agg = agg;
-  r.rank[0] = pre + inc - cnt;
+  const uint32_t g0 = tot & 0xFFFF, g1 = tot >> 16;
+  const uint32_t x = pre + inc - p;
+  r.agg = g0 + g1;
+  r.rank[0] = x & 0xFFFF;
+  r.rank[1] = g0 + (x >> 16);
   return r;
 }
 
 template <typename Put>
 __device__ inline void for_each_escape_e5m2(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put) {
   const uint32_t tid = threadIdx.x;
-  const uint64_t e0 = tile * kEncTile + 32 * tid;
-  const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTile + 32 * tid;
-  uint32_t m = r.mask[0];
-  uint32_t k = r.rank[0];
-  while (m) {
-    const uint32_t j = __builtin_ctz(m);
-    m &= m - 1;
-    put(k++, in_chunk + j, (uint32_t)(a.in[e0 + j] >> 2) & 0x1F);
+  const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTile;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    uint32_t m = r.mask[g];
+    uint32_t k = r.rank[g];
+    const uint64_t e0 = tile * kEncTile + g * 4096 + 16 * tid;
+    while (m) {
+      const uint32_t j = __builtin_ctz(m);
+      m &= m - 1;
+      put(k++, in_chunk + g * 4096 + 16 * tid + j, (uint32_t)(a.in[e0 + j] >> 2) & 0x1F);
+    }
   }
 }
 
@@ -721,19 +757,31 @@ __device__ inline void report_corrupt(int32_t* status) {
 
 __device__ inline uint32_t record_pos(const uint8_t* rec) { return rec[0] | ((uint32_t)rec[1] << 8); }
 
-// First record index in [lo, hi) whose position is >= key (positions are
-// ascending in a valid stream; a corrupt order is caught by the caller).
-__device__ uint64_t lower_bound_pos(const uint8_t* esc, uint64_t lo, uint64_t hi, uint32_t key) {
-  while (lo < hi) {
-    const uint64_t mid = lo + (hi - lo) / 2;
-    if (record_pos(esc + 3 * mid) < key) lo = mid + 1;
-    else hi = mid;
+// Smallest index i in [lo, hi] with i == hi or position(i) >= key (positions
+// ascend in a valid stream; a corrupt order is caught by the caller).  Run by
+// one full wave as a 64-way search: each round probes 64 evenly spaced
+// records at once and keeps the bucket holding the first hit, so a range of
+// L records takes ceil(log64(L + 1)) dependent loads instead of log2(L).
+__device__ uint64_t wave_lower_bound(const uint8_t* esc, uint64_t lo, uint64_t hi, uint32_t key) {
+  const uint64_t lane = __lane_id();
+  while (hi - lo > 63) {
+    const uint64_t step = (hi - lo + 63) / 64;  // 64 * step >= hi - lo: probe 64 hits hi
+    const uint64_t p = lo + (lane + 1) * step;
+    const bool hit = p >= hi || record_pos(esc + 3 * p) >= key;
+    const uint32_t i = (uint32_t)__builtin_ctzll(__ballot(hit));  // probe lo + (i + 1) step is the first hit
+    const uint64_t new_hi = std::min<uint64_t>(lo + (uint64_t)(i + 1) * step, hi);
+    lo = i == 0 ? lo : lo + (uint64_t)i * step + 1;                 // probe lo + i step missed
+    hi = new_hi;
   }
-  return lo;
+  const uint64_t p = lo + lane;  // hi - lo <= 63: lane hi - lo sees p == hi
+  const bool hit = p >= hi || record_pos(esc + 3 * p) >= key;
+  return lo + (uint64_t)__builtin_ctzll(__ballot(hit));
 }
 
 // Stage this tile's escapes in LDS: a bitmap over the tile's elements and
-// the raw exponents.  Returns false (uniformly) if the stream is invalid.
+// the raw exponents.  Every record of the chunk is checked by exactly one of
+// the chunk's tiles (in window, strictly increasing, valid value).  Returns
+// false (the same in every thread) if the stream is invalid.
 __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, uint32_t* bitmap, uint8_t* vals,
                               uint32_t* s_range, int* s_err) {
   const uint32_t tid = threadIdx.x;
@@ -751,11 +799,15 @@ __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, 
   if (!ok) return false;  // uniform: every thread read the same words
 
   for (uint32_t i = tid; i < kDecTile / 32; i += kThreads) bitmap[i] = 0;
-  if (tid == 0) {
-    s_range[0] = (uint32_t)((q == 0 ? lo : lower_bound_pos(a.in + h.s.esc, lo, hi, win_lo)) - lo);
-    *s_err = 0;
+  if (tid == 0) *s_err = 0;
+  // this tile's records: wave 0 finds the first, wave 1 the end
+  if (tid < 64) {
+    const uint64_t r = q == 0 ? lo : wave_lower_bound(a.in + h.s.esc, lo, hi, win_lo);
+    if (tid == 0) s_range[0] = (uint32_t)(r - lo);
+  } else if (tid < 128) {
+    const uint64_t r = last_in_chunk ? hi : wave_lower_bound(a.in + h.s.esc, lo, hi, win_lo + win_len);
+    if (tid == 64) s_range[1] = (uint32_t)(r - lo);
   }
-  if (tid == 64) s_range[1] = (uint32_t)((last_in_chunk ? hi : lower_bound_pos(a.in + h.s.esc, lo, hi, win_lo + win_len)) - lo);
   __syncthreads();
   const uint64_t ra = lo + s_range[0], rb = lo + s_range[1];
   const uint32_t vmax = a.dtype == SPLITZIP_BF16 ? 256u : 32u;
@@ -779,6 +831,9 @@ __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, 
   return *s_err == 0;
 }
 
+// BF16 decode tile: 16384 elements = 8 groups of 2048; thread t owns elements
+// 8t..8t+7 of each group (4 nibble bytes, 8 sign|mantissa bytes, 16 output
+// bytes; lane-contiguous across a wave).
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
   __shared__ uint32_t bitmap[kDecTile / 32];
   __shared__ uint8_t vals[kDecTile];
@@ -851,7 +906,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
       else e_hi = (e_hi & ~(0xFFu << sh)) | (v << sh);
     }
     uint32_t o[4];
-    #pragma unroll
+#pragma unroll
     for (int half = 0; half < 2; ++half) {
       const uint32_t e = half ? e_hi : e_lo;
       const uint32_t m = half ? sm.y : sm.x;
@@ -861,7 +916,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
       o[2 * half + 1] = perm(hi, lo, 0x07030602u);
     }
     if (valid == 8) {
-      *reinterpret_cast<uint4*>(out16 + e0) = make_uint4(o[0], o[1], o[2], o[3]);
+      store_stream(out16 + e0, make_uint4(o[0], o[1], o[2], o[3]));
     } else {
       for (uint32_t j = 0; j < valid; ++j)
         out16[e0 + j] = (uint16_t)(pick4(o[0], o[1], o[2], o[3], j >> 1) >> (16 * (j & 1)));
@@ -869,6 +924,17 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
   }
 }
 
+// Four E5M2 values from four 4-bit-code lookups (bytes of e) and 12 bits of
+// sign|mantissa triples.
+__device__ inline uint32_t e5m2_word(uint32_t e, uint32_t v12) {
+  const uint32_t y = (v12 & 0x3Fu) | ((v12 & 0xFC0u) << 10);
+  const uint32_t z = (y & 0x00070007u) | ((y << 5) & 0x07000700u);  // triple k in byte k
+  return ((z & 0x04040404u) << 5) | (e << 2) | (z & 0x03030303u);
+}
+
+// E5M2 decode tile: 16384 elements = 4 groups of 4096; thread t owns
+// elements 16t..16t+15 of each group (8 nibble bytes, 6 sign|mantissa bytes,
+// 16 output bytes; lane-contiguous across a wave).
 __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
   __shared__ uint32_t bitmap[kDecTile / 32];
   __shared__ uint8_t vals[kDecTile];
@@ -889,18 +955,19 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
   const uint8_t* cb = a.in + 64 + 16 * cbi;
   const uint32_t tid = threadIdx.x;
   const uint64_t first = tile * kDecTile;
-  // issue the tile's dense loads first: the escape staging overlaps them
-  uint4 pn[2];
-  uint32_t ps[2][3];
+  // issue the tile's dense loads first: the escape staging overlaps them.  A
+  // group takes the fast path when the next group exists too, so the second
+  // sign|mantissa dword never reaches past the section's data.
+  uint2 pn[4];
+  uint32_t p0[4], p1[4];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const uint64_t e0 = first + g * 8192 + 32 * tid;
+  for (int g = 0; g < 4; ++g) {
+    const uint64_t e0 = first + g * 4096 + 16 * tid;
     if (e0 + 32 <= a.n) {
-      const uint64_t smo = h.s.sm + 3 * (e0 / 8);
-      pn[g] = *reinterpret_cast<const uint4*>(a.in + h.s.nib + e0 / 2);
-      ps[g][0] = ld32(a.in + smo);
-      ps[g][1] = ld32(a.in + smo + 4);
-      ps[g][2] = ld32(a.in + smo + 8);
+      const uint64_t b = h.s.sm + 6 * (e0 / 16);
+      pn[g] = *reinterpret_cast<const uint2*>(a.in + h.s.nib + e0 / 2);
+      p0[g] = ld32(a.in + (b & ~uint64_t(3)));
+      p1[g] = ld32(a.in + (b & ~uint64_t(3)) + 4);
     }
   }
   const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4), l2 = ld32(cb + 8), l3 = ld32(cb + 12);
@@ -913,36 +980,33 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
     return;
   }
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const uint32_t local = g * 8192 + 32 * tid;
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t local = g * 4096 + 16 * tid;
     const uint64_t e0 = first + local;
     if (e0 >= a.n) break;
-    const uint32_t valid = (uint32_t)std::min<uint64_t>(32, a.n - e0);
-    uint32_t nib[4], sw[3];
-    const uint64_t smo = h.s.sm + 3 * (e0 / 8);
-    if (valid == 32) {
-      nib[0] = pn[g].x; nib[1] = pn[g].y; nib[2] = pn[g].z; nib[3] = pn[g].w;
-      sw[0] = ps[g][0];
-      sw[1] = ps[g][1];
-      sw[2] = ps[g][2];
+    const uint32_t valid = (uint32_t)std::min<uint64_t>(16, a.n - e0);
+    const uint64_t b = h.s.sm + 6 * (e0 / 16);
+    uint2 nib;
+    uint64_t v48;
+    if (e0 + 32 <= a.n) {
+      nib = pn[g];
+      v48 = ((((uint64_t)p1[g]) << 32) | p0[g]) >> (8 * (b & 3));
     } else {
-      const uint32_t nb = (valid + 1) / 2, sb = 3 * ((valid + 7) / 8);
-      #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        nib[k] = 0;
-        for (uint32_t b = 0; b < 4 && 4 * k + b < nb; ++b) nib[k] |= (uint32_t)a.in[h.s.nib + e0 / 2 + 4 * k + b] << (8 * b);
+      uint32_t n0 = 0, n1 = 0;
+      for (uint32_t k = 0; k < (valid + 1) / 2; ++k) {
+        const uint32_t x = (uint32_t)a.in[h.s.nib + e0 / 2 + k] << (8 * (k & 3));
+        if (k < 4) n0 |= x;
+        else n1 |= x;
       }
-      #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        sw[k] = 0;
-        for (uint32_t b = 0; b < 4 && 4 * k + b < sb; ++b) sw[k] |= (uint32_t)a.in[smo + 4 * k + b] << (8 * b);
-      }
+      nib = make_uint2(n0, n1);
+      v48 = 0;
+      for (uint32_t k = 0; k < 3 * ((valid + 7) / 8); ++k) v48 |= (uint64_t)a.in[b + k] << (8 * k);
     }
-    const uint32_t esc_bits = bitmap[local >> 5];
-    uint32_t o[8];
-    #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t e = lut4(spread4(nib[k >> 1], k & 1), l0, l1, l2, l3);
+    const uint32_t esc_bits = (bitmap[local >> 5] >> (local & 31)) & 0xFFFFu;
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t e = lut4(spread4(k < 2 ? nib.x : nib.y, k & 1), l0, l1, l2, l3);
       uint32_t mk = (esc_bits >> (4 * k)) & 0xFu;
       while (mk) {  // escape overwrite of elements 4k..4k+3
         const uint32_t j = __builtin_ctz(mk);
@@ -950,26 +1014,15 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
         const uint32_t sh = 8 * j;
         e = (e & ~(0xFFu << sh)) | ((uint32_t)vals[local + 4 * k + j] << sh);
       }
-      // 12 bits of sign|mantissa triples for elements 4k..4k+3
-      const int bit = 12 * k;
-      const int word = bit >> 5, sh = bit & 31;
-      const uint32_t hiw = word + 1 < 3 ? sw[word + 1] : 0u;
-      const uint32_t v12 = (uint32_t)(((((uint64_t)hiw) << 32) | sw[word]) >> sh) & 0xFFFu;
-      const uint32_t y = (v12 & 0x3Fu) | ((v12 & 0xFC0u) << 10);
-      const uint32_t z = (y & 0x00070007u) | ((y << 5) & 0x07000700u);
-      o[k] = ((z & 0x04040404u) << 5) | (e << 2) | (z & 0x03030303u);
+      o[k] = e5m2_word(e, (uint32_t)(v48 >> (12 * k)) & 0xFFFu);
     }
-    if (valid == 32) {
-      *reinterpret_cast<uint4*>(a.out + e0) = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4*>(a.out + e0 + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+    if (valid == 16) {
+      store_stream(a.out + e0, make_uint4(o[0], o[1], o[2], o[3]));
     } else {
-      #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        for (uint32_t b = 0; b < 4 && 4 * k + b < valid; ++b) a.out[e0 + 4 * k + b] = (uint8_t)(o[k] >> (8 * b));
+      for (uint32_t j = 0; j < valid; ++j) a.out[e0 + j] = (uint8_t)(pick4(o[0], o[1], o[2], o[3], j >> 2) >> (8 * (j & 3)));
     }
   }
 }
-
 
 // ------------------------------------------------------------ host helpers
 bool dtype_valid(int dtype) { return dtype == SPLITZIP_BF16 || dtype == SPLITZIP_FP8_E5M2; }
