@@ -41,7 +41,8 @@ namespace {
 constexpr uint64_t kChunk = 65536;
 constexpr int kThreads = 256;
 constexpr uint64_t kEncTile = 8192;   // elements per encode workgroup
-constexpr uint64_t kDecTile = 16384;  // elements per decode workgroup
+constexpr uint32_t kDecTileBf16 = 16384;  // elements per decode workgroup
+constexpr uint32_t kDecTileE5m2 = 16384;
 constexpr uint32_t kMagic = 0x00315A53u;
 constexpr uint32_t kMaxK = 65535;
 constexpr uint64_t kMaxN = 1ull << 40;
@@ -157,6 +158,13 @@ __device__ inline uint32_t pick4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t
 __device__ inline uint32_t flag_mask4(uint32_t codes) {
   const uint32_t t = (codes >> 4) & 0x01010101u;
   return ((t * 0x01020408u) >> 24) & 0xFu;
+}
+
+// Byte mask of four flag bits: bit k of f (k < 4) -> 0xFF in byte k.  The
+// product moves bit k to bit 8k (the shifted copies never collide below
+// bit 25), and perm selector 12 / 13 yields 0x00 / 0xFF.
+__device__ inline uint32_t byte_mask4(uint32_t f) {
+  return perm(0u, 0u, ((f * 0x00204081u) & 0x01010101u) | 0x0C0C0C0Cu);
 }
 
 __device__ inline uint32_t keep_low_bytes(uint32_t nbytes) {
@@ -782,6 +790,7 @@ __device__ uint64_t wave_lower_bound(const uint8_t* esc, uint64_t lo, uint64_t h
 // the raw exponents.  Every record of the chunk is checked by exactly one of
 // the chunk's tiles (in window, strictly increasing, valid value).  Returns
 // false (the same in every thread) if the stream is invalid.
+template <uint32_t kDecTile>
 __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, uint32_t* bitmap, uint8_t* vals,
                               uint32_t* s_range, int* s_err) {
   const uint32_t tid = threadIdx.x;
@@ -835,8 +844,9 @@ __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, 
 // 8t..8t+7 of each group (4 nibble bytes, 8 sign|mantissa bytes, 16 output
 // bytes; lane-contiguous across a wave).
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
+  constexpr uint32_t kDecTile = kDecTileBf16, kGroups = kDecTile / 2048;
   __shared__ uint32_t bitmap[kDecTile / 32];
-  __shared__ uint8_t vals[kDecTile];
+  __shared__ alignas(16) uint8_t vals[kDecTile];
   __shared__ uint32_t s_range[2];
   __shared__ int s_err;
   Header h;
@@ -855,10 +865,10 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
   const uint32_t tid = threadIdx.x;
   const uint64_t first = tile * kDecTile;
   // issue the tile's dense loads first: the escape staging overlaps them
-  uint32_t nibs[8];
-  uint2 sms[8];
+  uint32_t nibs[kGroups];
+  uint2 sms[kGroups];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
+  for (uint32_t g = 0; g < kGroups; ++g) {
     const uint64_t e0 = first + g * 2048 + 8 * tid;
     if (e0 + 8 <= a.n) {
       nibs[g] = ld32(a.in + h.s.nib + e0 / 2);
@@ -866,14 +876,14 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
     }
   }
   const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4), l2 = ld32(cb + 8), l3 = ld32(cb + 12);
-  if (!stage_escapes(a, h, tile, bitmap, vals, s_range, &s_err)) {
+  if (!stage_escapes<kDecTile>(a, h, tile, bitmap, vals, s_range, &s_err)) {
     if (threadIdx.x == 0) report_corrupt(a.status);
     return;
   }
   const uint8_t* bm8 = reinterpret_cast<const uint8_t*>(bitmap);
   uint16_t* out16 = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
+  for (uint32_t g = 0; g < kGroups; ++g) {
     const uint32_t local = g * 2048 + 8 * tid;
     const uint64_t e0 = first + local;
     if (e0 >= a.n) break;
@@ -896,14 +906,15 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
     }
     uint32_t e_lo = lut4(spread4(nib, 0), l0, l1, l2, l3);
     uint32_t e_hi = lut4(spread4(nib, 1), l0, l1, l2, l3);
-    uint32_t mask = bm8[local >> 3];
-    while (mask) {  // escape overwrite, before the values are assembled
-      const uint32_t j = __builtin_ctz(mask);
-      mask &= mask - 1;
-      const uint32_t v = vals[local + j];
-      const uint32_t sh = 8 * (j & 3);
-      if (j < 4) e_lo = (e_lo & ~(0xFFu << sh)) | (v << sh);
-      else e_hi = (e_hi & ~(0xFFu << sh)) | (v << sh);
+    // escape overwrite, before the values are assembled: the raw exponents
+    // replace the looked-up bytes where the bitmap is set (vals bytes of
+    // elements without an escape are never used)
+    const uint32_t mask = bm8[local >> 3];
+    if (mask) {
+      const uint2 v = *reinterpret_cast<const uint2*>(vals + local);
+      const uint32_t m_lo = byte_mask4(mask & 0xFu), m_hi = byte_mask4(mask >> 4);
+      e_lo = (e_lo & ~m_lo) | (v.x & m_lo);
+      e_hi = (e_hi & ~m_hi) | (v.y & m_hi);
     }
     uint32_t o[4];
 #pragma unroll
@@ -924,20 +935,56 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
   }
 }
 
-// Four E5M2 values from four 4-bit-code lookups (bytes of e) and 12 bits of
-// sign|mantissa triples.
-__device__ inline uint32_t e5m2_word(uint32_t e, uint32_t v12) {
-  const uint32_t y = (v12 & 0x3Fu) | ((v12 & 0xFC0u) << 10);
-  const uint32_t z = (y & 0x00070007u) | ((y << 5) & 0x07000700u);  // triple k in byte k
-  return ((z & 0x04040404u) << 5) | (e << 2) | (z & 0x03030303u);
+// E5M2 decode of 16 elements: the 16 codes (8 nibble bytes) through the
+// code-pair table (entry = exponent of the low code << 2 | exponent of the
+// high code << 10, i.e. two output bytes' exponent fields), and the 16
+// sign|mantissa triples (bits 0..47 of lo:hi, element j at bit 3j).  The
+// triples of word k (elements 4k..4k+3) are spread to one per byte in two
+// steps (pairs to 16-bit halves, then triples to bytes); t + (t << 5) keeps
+// the mantissa in bits 0..1 and moves the sign to bit 7 (no carries: t < 8).
+__device__ inline uint32_t e5m2_spread(uint32_t y) {  // y: pairs at bits 0..5, 16..21
+  const uint32_t z = (y & 0x00070007u) | ((y << 5) & 0x07000700u);
+  return (z + (z << 5)) & 0x83838383u;
+}
+
+__device__ inline uint4 e5m2_decode16(const uint16_t* tab2, uint2 nib, uint32_t lo, uint32_t hi) {
+  const uint32_t e0 = tab2[nib.x & 0xFF] | ((uint32_t)tab2[(nib.x >> 8) & 0xFF] << 16);
+  const uint32_t e1 = tab2[(nib.x >> 16) & 0xFF] | ((uint32_t)tab2[nib.x >> 24] << 16);
+  const uint32_t e2 = tab2[nib.y & 0xFF] | ((uint32_t)tab2[(nib.y >> 8) & 0xFF] << 16);
+  const uint32_t e3 = tab2[(nib.y >> 16) & 0xFF] | ((uint32_t)tab2[nib.y >> 24] << 16);
+  const uint32_t y0 = (lo & 0x3Fu) | ((lo << 10) & 0x3F0000u);
+  const uint32_t y1 = ((lo >> 12) & 0x3Fu) | ((lo >> 2) & 0x3F0000u);
+  const uint32_t y2 = ((lo >> 24) & 0x3Fu) | (__builtin_amdgcn_alignbit(hi, lo, 14) & 0x3F0000u);
+  const uint32_t y3 = ((hi >> 4) & 0x3Fu) | ((hi << 6) & 0x3F0000u);
+  return make_uint4(e5m2_spread(y0) | e0, e5m2_spread(y1) | e1, e5m2_spread(y2) | e2, e5m2_spread(y3) | e3);
+}
+
+// Raw exponents of escaped elements replace the looked-up ones: esc16 holds
+// one flag per element, v the 16 staged bytes (bytes of elements without an
+// escape are never used).
+__device__ inline uint32_t e5m2_patch4(uint32_t w, uint32_t esc4, uint32_t v) {
+  const uint32_t m = byte_mask4(esc4);
+  return (w & ~(m & 0x7C7C7C7Cu)) | ((v & m) << 2);
+}
+
+__device__ inline void e5m2_patch16(uint4& o, uint32_t esc16, uint4 v) {
+  o.x = e5m2_patch4(o.x, esc16 & 0xFu, v.x);
+  o.y = e5m2_patch4(o.y, (esc16 >> 4) & 0xFu, v.y);
+  o.z = e5m2_patch4(o.z, (esc16 >> 8) & 0xFu, v.z);
+  o.w = e5m2_patch4(o.w, esc16 >> 12, v.w);
 }
 
 // E5M2 decode tile: 16384 elements = 4 groups of 4096; thread t owns
 // elements 16t..16t+15 of each group (8 nibble bytes, 6 sign|mantissa bytes,
-// 16 output bytes; lane-contiguous across a wave).
+// 16 output bytes; lane-contiguous across a wave).  A whole tile takes the
+// fast path: no bounds checks, and each thread's two aligned sign|mantissa
+// dwords stay inside the tile's bytes (6t mod 4 is 0 or 2, and the last
+// thread is odd).
 __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
+  constexpr uint32_t kDecTile = kDecTileE5m2, kGroups = kDecTile / 4096;
   __shared__ uint32_t bitmap[kDecTile / 32];
-  __shared__ uint8_t vals[kDecTile];
+  __shared__ alignas(16) uint8_t vals[kDecTile];
+  __shared__ uint16_t tab2[256];
   __shared__ uint32_t s_range[2];
   __shared__ int s_err;
   Header h;
@@ -955,19 +1002,19 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
   const uint8_t* cb = a.in + 64 + 16 * cbi;
   const uint32_t tid = threadIdx.x;
   const uint64_t first = tile * kDecTile;
-  // issue the tile's dense loads first: the escape staging overlaps them.  A
-  // group takes the fast path when the next group exists too, so the second
-  // sign|mantissa dword never reaches past the section's data.
-  uint2 pn[4];
-  uint32_t p0[4], p1[4];
+  const bool fast = first + kDecTile <= a.n;  // same in every thread
+  const uint8_t* nib_t = a.in + h.s.nib + first / 2;
+  const uint8_t* sm_t = a.in + h.s.sm + 3 * (first / 8);
+  // issue the tile's dense loads first: the escape staging overlaps them
+  uint2 pn[kGroups];
+  uint32_t p0[kGroups], p1[kGroups];
+  if (fast) {
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const uint64_t e0 = first + g * 4096 + 16 * tid;
-    if (e0 + 32 <= a.n) {
-      const uint64_t b = h.s.sm + 6 * (e0 / 16);
-      pn[g] = *reinterpret_cast<const uint2*>(a.in + h.s.nib + e0 / 2);
-      p0[g] = ld32(a.in + (b & ~uint64_t(3)));
-      p1[g] = ld32(a.in + (b & ~uint64_t(3)) + 4);
+    for (uint32_t g = 0; g < kGroups; ++g) {
+      pn[g] = *reinterpret_cast<const uint2*>(nib_t + g * 2048 + 8 * tid);
+      const uint8_t* s = sm_t + g * 1536 + ((6 * tid) & ~3u);
+      p0[g] = ld32(s);
+      p1[g] = ld32(s + 4);
     }
   }
   const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4), l2 = ld32(cb + 8), l3 = ld32(cb + 12);
@@ -975,52 +1022,48 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
     if (threadIdx.x == 0) report_corrupt(a.status);
     return;
   }
-  if (!stage_escapes(a, h, tile, bitmap, vals, s_range, &s_err)) {
+  {  // code-pair table entry tid: codes tid & 15 (even element) and tid >> 4
+    const uint32_t c = tid & 0xFFu;
+    const uint32_t pair = lut4((c & 0xFu) | ((c >> 4) << 8), l0, l1, l2, l3);  // bytes 0, 1: the two exponents
+    tab2[c] = (uint16_t)((pair & 0xFFu) << 2 | ((pair >> 8) & 0xFFu) << 10);
+  }
+  if (!stage_escapes<kDecTile>(a, h, tile, bitmap, vals, s_range, &s_err)) {  // its barriers publish tab2
     if (threadIdx.x == 0) report_corrupt(a.status);
     return;
   }
+  if (fast) {
+    uint8_t* out_t = a.out + first;
+    const uint32_t sh = (tid & 1u) * 16;  // 6t mod 4 = 2 (t & 1)
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+    for (uint32_t g = 0; g < kGroups; ++g) {
+      const uint32_t local = g * 4096 + 16 * tid;
+      uint4 o = e5m2_decode16(tab2, pn[g], __builtin_amdgcn_alignbit(p1[g], p0[g], sh), p1[g] >> sh);
+      const uint32_t esc16 = (bitmap[local >> 5] >> (local & 31)) & 0xFFFFu;
+      if (esc16) e5m2_patch16(o, esc16, *reinterpret_cast<const uint4*>(vals + local));
+      store_stream(out_t + local, o);
+    }
+    return;
+  }
+  // last tile: byte-wise loads and stores
+#pragma unroll 1
+  for (uint32_t g = 0; g < kGroups; ++g) {
     const uint32_t local = g * 4096 + 16 * tid;
     const uint64_t e0 = first + local;
     if (e0 >= a.n) break;
     const uint32_t valid = (uint32_t)std::min<uint64_t>(16, a.n - e0);
-    const uint64_t b = h.s.sm + 6 * (e0 / 16);
-    uint2 nib;
-    uint64_t v48;
-    if (e0 + 32 <= a.n) {
-      nib = pn[g];
-      v48 = ((((uint64_t)p1[g]) << 32) | p0[g]) >> (8 * (b & 3));
-    } else {
-      uint32_t n0 = 0, n1 = 0;
-      for (uint32_t k = 0; k < (valid + 1) / 2; ++k) {
-        const uint32_t x = (uint32_t)a.in[h.s.nib + e0 / 2 + k] << (8 * (k & 3));
-        if (k < 4) n0 |= x;
-        else n1 |= x;
-      }
-      nib = make_uint2(n0, n1);
-      v48 = 0;
-      for (uint32_t k = 0; k < 3 * ((valid + 7) / 8); ++k) v48 |= (uint64_t)a.in[b + k] << (8 * k);
+    uint32_t n0 = 0, n1 = 0;
+    for (uint32_t k = 0; k < (valid + 1) / 2; ++k) {
+      const uint32_t x = (uint32_t)nib_t[local / 2 + k] << (8 * (k & 3));
+      if (k < 4) n0 |= x;
+      else n1 |= x;
     }
-    const uint32_t esc_bits = (bitmap[local >> 5] >> (local & 31)) & 0xFFFFu;
-    uint32_t o[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t e = lut4(spread4(k < 2 ? nib.x : nib.y, k & 1), l0, l1, l2, l3);
-      uint32_t mk = (esc_bits >> (4 * k)) & 0xFu;
-      while (mk) {  // escape overwrite of elements 4k..4k+3
-        const uint32_t j = __builtin_ctz(mk);
-        mk &= mk - 1;
-        const uint32_t sh = 8 * j;
-        e = (e & ~(0xFFu << sh)) | ((uint32_t)vals[local + 4 * k + j] << sh);
-      }
-      o[k] = e5m2_word(e, (uint32_t)(v48 >> (12 * k)) & 0xFFFu);
-    }
-    if (valid == 16) {
-      store_stream(a.out + e0, make_uint4(o[0], o[1], o[2], o[3]));
-    } else {
-      for (uint32_t j = 0; j < valid; ++j) a.out[e0 + j] = (uint8_t)(pick4(o[0], o[1], o[2], o[3], j >> 2) >> (8 * (j & 3)));
-    }
+    uint64_t v48 = 0;
+    const uint8_t* s = sm_t + 6 * (local / 16);
+    for (uint32_t k = 0; k < 3 * ((valid + 7) / 8); ++k) v48 |= (uint64_t)s[k] << (8 * k);
+    uint4 o = e5m2_decode16(tab2, make_uint2(n0, n1), (uint32_t)v48, (uint32_t)(v48 >> 32));
+    const uint32_t esc16 = (bitmap[local >> 5] >> (local & 31)) & 0xFFFFu;
+    if (esc16) e5m2_patch16(o, esc16, *reinterpret_cast<const uint4*>(vals + local));
+    for (uint32_t j = 0; j < valid; ++j) a.out[e0 + j] = (uint8_t)(pick4(o.x, o.y, o.z, o.w, j >> 2) >> (8 * (j & 3)));
   }
 }
 
@@ -1155,13 +1198,12 @@ int splitzip_decompress(const void* d_in, size_t in_bytes, int dtype, size_t n_e
   a.n = n_elems;
   a.status = d_status;
   a.dtype = dtype;
-  // one workgroup per 16384-element tile; a header-only stream (n == 0)
-  // still gets one workgroup, which only validates
-  const uint32_t blocks = (uint32_t)std::max<uint64_t>(1, divup(n_elems, kDecTile));
+  // one workgroup per tile; a header-only stream (n == 0) still gets one
+  // workgroup, which only validates
   if (dtype == SPLITZIP_BF16) {
-    decode_bf16_kernel<<<blocks, kThreads, 0, stream>>>(a);
+    decode_bf16_kernel<<<(uint32_t)std::max<uint64_t>(1, divup(n_elems, kDecTileBf16)), kThreads, 0, stream>>>(a);
   } else {
-    decode_e5m2_kernel<<<blocks, kThreads, 0, stream>>>(a);
+    decode_e5m2_kernel<<<(uint32_t)std::max<uint64_t>(1, divup(n_elems, kDecTileE5m2)), kThreads, 0, stream>>>(a);
   }
   if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
   return SPLITZIP_OK;
