@@ -269,6 +269,9 @@ constexpr uint32_t kBlockTiles = 64;  // tiles per encode_place workgroup
 
 struct EncShared {
   uint8_t table[256];
+  // E5M2: word for input byte b at byte position j of a 4-element word:
+  // code << 4j | (sign << 2 | mantissa) << (16 + 3j) | escaped << (28 + j)
+  uint32_t pos4[4 * 256];
   uint32_t wave[8];
   uint64_t red[16];
   alignas(16) uint32_t s3[4 * 96];  // E5M2: a wave's 64 x 6 sign|mantissa bytes, gathered for aligned stores
@@ -306,6 +309,15 @@ __device__ inline void build_table(const EncArgs& a, EncShared& sh, uint64_t cbi
   __syncthreads();
   if (tid < 16) sh.table[a.out[64 + 16 * cbi + tid]] = (uint8_t)tid;
   __syncthreads();
+  if (entries == 32) {  // E5M2 per-position words, from the exponent table
+    const uint32_t b = tid & 0xFFu;
+    const uint32_t c = sh.table[(b >> 2) & 0x1Fu];
+    const uint32_t code = c & 0xFu, esc = c >> 4;  // kEsc: code 0, escaped
+    const uint32_t tri = ((b >> 5) & 4u) | (b & 3u);
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) sh.pos4[256 * j + b] = (code << (4 * j)) | (tri << (16 + 3 * j)) | (esc << (28 + j));
+    __syncthreads();
+  }
 }
 
 // Per-thread escape bookkeeping of one tile: element-order rank of the
@@ -446,82 +458,86 @@ __device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, con
   }
 }
 
-// Four E5M2 bytes -> their 3-bit sign|mantissa values packed into 12 bits.
-__device__ inline uint32_t signmant12(uint32_t w) {
-  // byte k -> 3-bit value sign<<2 | mantissa, then 4 x 3 bits -> 12 bits
-  const uint32_t u = ((w >> 5) & 0x04040404u) | (w & 0x03030303u);
-  const uint32_t v = u | (u >> 5);  // bits 0..5: e0|e1<<3 ; bits 16..21: e2|e3<<3
-  return (v & 0x3Fu) | ((v >> 10) & 0xFC0u);
-}
-
 // E5M2 tile: 8192 elements = 2 groups of 4096; thread t owns elements
 // 16t..16t+15 of each group: 16 input bytes, 8 nibble bytes and 6
 // sign|mantissa bytes, all lane-contiguous across a wave.
 __device__ inline TileIn load_tile_e5m2(const EncArgs& a, uint64_t tile) {
   TileIn in;
+  const uint32_t tid = threadIdx.x;
+  const uint64_t first = tile * kEncTile;
+  const uint8_t* src = a.in + first;
+  if (first + kEncTile <= a.n) {  // same in every thread
+#pragma unroll
+    for (int g = 0; g < 2; ++g) in.w[g] = *reinterpret_cast<const uint4*>(src + g * 4096 + 16 * tid);
+    return in;
+  }
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const uint64_t e0 = tile * kEncTile + g * 4096 + 16 * threadIdx.x;
-    const uint32_t valid = valid_in_group(a.n, e0, 16);
-    if (valid == 16) {
-      in.w[g] = *reinterpret_cast<const uint4*>(a.in + e0);
-    } else {
-      uint32_t v[4] = {0, 0, 0, 0};
+    const uint32_t local = g * 4096 + 16 * tid;
+    const uint32_t valid = valid_in_group(a.n, first + local, 16);
+    uint32_t v[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        for (uint32_t b = 0; b < 4 && 4 * k + b < valid; ++b) v[k] |= (uint32_t)a.in[e0 + 4 * k + b] << (8 * b);
-      in.w[g] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
+    for (int k = 0; k < 4; ++k)
+      for (uint32_t b = 0; b < 4 && 4 * k + b < valid; ++b) v[k] |= (uint32_t)src[local + 4 * k + b] << (8 * b);
+    in.w[g] = make_uint4(v[0], v[1], v[2], v[3]);
   }
   return in;
 }
 
+// Per-position table words of the four bytes of x, OR-ed: nibble codes of
+// the four elements in bits 0..15, their triples in bits 16..27, escape
+// flags in bits 28..31.
+__device__ inline uint32_t e5m2_pos_word(const uint32_t* pos4, uint32_t x) {
+  return pos4[x & 0xFFu] | pos4[256 + ((x >> 8) & 0xFFu)] | pos4[512 + ((x >> 16) & 0xFFu)] | pos4[768 + (x >> 24)];
+}
+
 __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store) {
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool tile_full = (tile + 1) * kEncTile <= a.n;  // same in every thread
+  const uint64_t first = tile * kEncTile;
+  const bool tile_full = first + kEncTile <= a.n;  // same in every thread
   TileEsc r;
   uint32_t cnt[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const uint64_t e0 = tile * kEncTile + g * 4096 + 16 * tid;
-    const uint32_t valid = valid_in_group(a.n, e0, 16);
-    const uint32_t w[4] = {in.w[g].x, in.w[g].y, in.w[g].z, in.w[g].w};
-    uint32_t c[4];
-    r.mask[g] = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t x = w[k];
-      const uint8_t* tb = sh.table;
-      c[k] = gather4(tb[(x >> 2) & 0x1F], tb[(x >> 10) & 0x1F], tb[(x >> 18) & 0x1F], tb[(x >> 26) & 0x1F]);
-      if (valid < 16) c[k] &= keep_low_bytes(valid > 4u * k ? valid - 4u * k : 0u);
-      r.mask[g] |= flag_mask4(c[k]) << (4 * k);
+    const uint32_t local = g * 4096 + 16 * tid;
+    const uint32_t r0 = e5m2_pos_word(sh.pos4, in.w[g].x), r1 = e5m2_pos_word(sh.pos4, in.w[g].y);
+    const uint32_t r2 = e5m2_pos_word(sh.pos4, in.w[g].z), r3 = e5m2_pos_word(sh.pos4, in.w[g].w);
+    // escape flags in element order, nibbles, 16 triples = 48 bits (element i at bit 3i)
+    uint32_t f = (r0 >> 28) | ((r1 >> 24) & 0xF0u) | ((r2 >> 20) & 0xF00u) | ((r3 >> 16) & 0xF000u);
+    uint2 nib = make_uint2(perm(r1, r0, 0x05040100u), perm(r3, r2, 0x05040100u));
+    uint32_t lo = ((r0 >> 16) & 0xFFFu) | ((r1 >> 4) & 0xFFF000u) | ((r2 << 8) & 0xFF000000u);
+    uint32_t hi = ((r2 >> 24) & 0xFu) | ((r3 >> 12) & 0xFFF0u);
+    uint32_t valid = 16;
+    if (!tile_full) {  // elements past n: no code, no triple, no escape
+      valid = valid_in_group(a.n, first + local, 16);
+      const uint64_t k48 = (1ull << (3 * valid)) - 1, k64 = valid >= 16 ? ~0ull : (1ull << (4 * valid)) - 1;
+      f &= (1u << valid) - 1u;
+      nib.x &= (uint32_t)k64;
+      nib.y &= (uint32_t)(k64 >> 32);
+      lo &= (uint32_t)k48;
+      hi &= (uint32_t)(k48 >> 32);
     }
-    cnt[g] = __builtin_popcount(r.mask[g]);
+    r.mask[g] = f;
+    cnt[g] = __builtin_popcount(f);
     if (!store) continue;
-    const uint2 nib = make_uint2(pack_nibbles(c[0], c[1]), pack_nibbles(c[2], c[3]));
-    // 16 triples = 48 bits, element i at bit 3i
-    const uint32_t s0 = signmant12(w[0]), s1 = signmant12(w[1]), s2 = signmant12(w[2]), s3 = signmant12(w[3]);
-    const uint32_t lo = s0 | (s1 << 12) | (s2 << 24);
-    const uint32_t hi = (s2 >> 8) | (s3 << 4);
-    const uint64_t smo = a.sm + 6 * (e0 / 16);
     if (tile_full) {
-      store_stream(a.out + a.nib + e0 / 2, nib);
-      // gather the wave's 64 x 6 bytes in LDS, then 24 aligned 16-byte stores
-      uint8_t* buf = reinterpret_cast<uint8_t*>(sh.s3 + wave * 96);
-      if ((lane & 1) == 0) {
-        *reinterpret_cast<uint32_t*>(buf + 6 * lane) = lo;
-        *reinterpret_cast<uint16_t*>(buf + 6 * lane + 4) = (uint16_t)hi;
-      } else {
-        *reinterpret_cast<uint16_t*>(buf + 6 * lane) = (uint16_t)lo;
-        *reinterpret_cast<uint32_t*>(buf + 6 * lane + 2) = (lo >> 16) | (hi << 16);
-      }
-      __syncthreads();
+      store_stream(a.out + a.nib + (first + local) / 2, nib);
+      // the wave's 64 x 6 sign|mantissa bytes go through its own LDS slice
+      // to 24 aligned 16-byte stores.  A wave's LDS operations complete in
+      // issue order, so only the compiler needs a barrier here.
+      uint16_t* buf = reinterpret_cast<uint16_t*>(sh.s3 + wave * 96);
+      buf[3 * lane] = (uint16_t)lo;
+      buf[3 * lane + 1] = (uint16_t)(lo >> 16);
+      buf[3 * lane + 2] = (uint16_t)hi;
+      asm volatile("" ::: "memory");
       if (lane < 24) {
-        const uint64_t wave_smo = a.sm + 6 * ((tile * kEncTile + g * 4096 + 1024 * wave) / 16);
-        store_stream(a.out + wave_smo + 16 * lane, *reinterpret_cast<const uint4*>(buf + 16 * lane));
+        const uint64_t wave_smo = a.sm + 6 * ((first + g * 4096 + 1024 * wave) / 16);
+        store_stream(a.out + wave_smo + 16 * lane, *reinterpret_cast<const uint4*>(sh.s3 + wave * 96 + 4 * lane));
       }
-      __syncthreads();
+      asm volatile("" ::: "memory");
     } else if (valid > 0) {
+      const uint64_t e0 = first + local;
+      const uint64_t smo = a.sm + 6 * (e0 / 16);
       for (uint32_t b = 0; b < (valid + 1) / 2; ++b)
         a.out[a.nib + e0 / 2 + b] = (uint8_t)((b < 4 ? nib.x : nib.y) >> (8 * (b & 3)));
       for (uint32_t b = 0; b < 3 * ((valid + 7) / 8); ++b)
@@ -575,8 +591,8 @@ template <bool kBf16>
 __device__ void encode_dense(const EncArgs& a) {
   __shared__ EncShared sh;
   const uint64_t t = blockIdx.x;
+  const TileIn in = kBf16 ? load_tile_bf16(a, t) : load_tile_e5m2(a, t);  // in flight during the table build
   build_table(a, sh, a.seg_chunks ? (t >> 3) / a.seg_chunks : 0, kBf16 ? 256u : 32u);
-  const TileIn in = kBf16 ? load_tile_bf16(a, t) : load_tile_e5m2(a, t);
   const TileEsc r = kBf16 ? encode_tile_bf16(a, sh, t, in, true) : encode_tile_e5m2(a, sh, t, in, true);
   if (threadIdx.x == 0) a.tile_count[t] = r.agg;
   if (r.agg <= kStageSlot) {
