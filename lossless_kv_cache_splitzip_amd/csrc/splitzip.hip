@@ -52,6 +52,13 @@ constexpr uint8_t kEsc = 0x10;  // table entry of an exponent outside the codebo
 __host__ __device__ inline uint64_t round256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 __host__ __device__ inline uint64_t divup(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
+// Codebook of chunk c when a segment spans seg_chunks > 0 chunks, in 32-bit
+// arithmetic (c < 2^24 since n <= 2^40); a 64-bit division would cost every
+// wave a long emulation.
+__device__ inline uint32_t codebook_of_chunk(uint64_t c, uint64_t seg_chunks) {
+  return seg_chunks > 0xFFFFFFFFull ? 0u : (uint32_t)c / (uint32_t)seg_chunks;
+}
+
 struct Sections {
   uint64_t chunks, offsets, nib, sm, esc, sm_bytes;
 };
@@ -180,13 +187,6 @@ __device__ inline uint32_t lut4(uint32_t s, uint32_t l0, uint32_t l1, uint32_t l
   // selector 12 yields 0x00, 13 yields 0xFF: a byte mask from code bit 3
   const uint32_t m = perm(0u, 0u, ((s >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
   return (hi & m) | (lo & ~m);
-}
-
-// Spread 4 nibbles (the 16 bits at bit offset 16*half of w) into 4 bytes
-// (low nibble of each byte valid, high nibble garbage).
-__device__ inline uint32_t spread4(uint32_t w, int half) {
-  const uint32_t t = perm(w, w, half ? 0x03030202u : 0x01010000u);
-  return (t & 0x000F000Fu) | ((t >> 4) & 0x0F000F00u);
 }
 
 // ------------------------------------------------------------- prep kernel
@@ -592,7 +592,7 @@ __device__ void encode_dense(const EncArgs& a) {
   __shared__ EncShared sh;
   const uint64_t t = blockIdx.x;
   const TileIn in = kBf16 ? load_tile_bf16(a, t) : load_tile_e5m2(a, t);  // in flight during the table build
-  build_table(a, sh, a.seg_chunks ? (t >> 3) / a.seg_chunks : 0, kBf16 ? 256u : 32u);
+  build_table(a, sh, a.seg_chunks ? codebook_of_chunk(t >> 3, a.seg_chunks) : 0, kBf16 ? 256u : 32u);
   const TileEsc r = kBf16 ? encode_tile_bf16(a, sh, t, in, true) : encode_tile_e5m2(a, sh, t, in, true);
   if (threadIdx.x == 0) a.tile_count[t] = r.agg;
   if (r.agg <= kStageSlot) {
@@ -712,7 +712,7 @@ __device__ void encode_place(const EncArgs& a) {
     const uint32_t n_i = sh.pre_all[i + 1] - sh.pre_all[i];
     if (n_i <= kStageSlot) continue;  // uniform
     const uint64_t tt = blk * kBlockTiles + i;
-    const uint64_t cbi = a.seg_chunks ? (tt >> 3) / a.seg_chunks : 0;
+    const uint64_t cbi = a.seg_chunks ? codebook_of_chunk(tt >> 3, a.seg_chunks) : 0;
     if (cbi != table_cb) {
       build_table(a, esh, cbi, kBf16 ? 256u : 32u);
       table_cb = cbi;
@@ -766,7 +766,7 @@ __device__ bool read_header(const DecArgs& a, Header& h) {
   if (h.k == 0 || h.k > kMaxK) return false;
   if (h.k == 1) {
     if (h.seg != a.n) return false;
-  } else if (h.seg == 0 || (h.seg % kChunk) != 0 || h.seg < divup(a.n, h.k)) {
+  } else if (h.seg == 0 || (h.seg % kChunk) != 0 || (h.seg < a.n && h.seg * h.k < a.n)) {  // seg >= ceil(n / k); k < 2^16
     return false;
   }
   if (h.e > a.n) return false;
@@ -856,13 +856,43 @@ __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, 
   return *s_err == 0;
 }
 
+// BF16 decode of 8 elements: the 8 codes (4 nibble bytes) through the
+// code-pair table (entry = exponent of the low code << 7 | exponent of the
+// high code << 23, i.e. the exponent fields of two output values) and the 8
+// sign|mantissa bytes: mantissa bits to bits 0..6 and the sign to bit 15 of
+// each value, by one byte permutation of the masked bytes.
+__device__ inline uint4 bf16_decode8(const uint32_t* tab2, uint32_t nib, uint2 sm) {
+  const uint32_t m0 = sm.x & 0x7F7F7F7Fu, s0 = sm.x & 0x80808080u;
+  const uint32_t m1 = sm.y & 0x7F7F7F7Fu, s1 = sm.y & 0x80808080u;
+  return make_uint4(perm(s0, m0, 0x05010400u) | tab2[nib & 0xFFu], perm(s0, m0, 0x07030602u) | tab2[(nib >> 8) & 0xFFu],
+                    perm(s1, m1, 0x05010400u) | tab2[(nib >> 16) & 0xFFu], perm(s1, m1, 0x07030602u) | tab2[nib >> 24]);
+}
+
+// Raw exponents of escaped elements replace the looked-up ones in the value
+// pair w (elements 2k, 2k+1): esc2 holds their flags, v2 their staged bytes
+// in bytes 0 and 1.
+__device__ inline uint32_t bf16_patch2(uint32_t w, uint32_t esc2, uint32_t v2) {
+  const uint32_t m = ((esc2 & 1u) ? 0x00007F80u : 0u) | ((esc2 & 2u) ? 0x7F800000u : 0u);
+  const uint32_t e = perm(0u, v2, 0x0C010C00u) << 7;  // byte 0 -> bits 7..14, byte 1 -> bits 23..30
+  return (w & ~m) | (e & m);
+}
+
+__device__ inline void bf16_patch8(uint4& o, uint32_t esc8, uint2 v) {
+  o.x = bf16_patch2(o.x, esc8 & 3u, v.x);
+  o.y = bf16_patch2(o.y, (esc8 >> 2) & 3u, v.x >> 16);
+  o.z = bf16_patch2(o.z, (esc8 >> 4) & 3u, v.y);
+  o.w = bf16_patch2(o.w, (esc8 >> 6) & 3u, v.y >> 16);
+}
+
 // BF16 decode tile: 16384 elements = 8 groups of 2048; thread t owns elements
 // 8t..8t+7 of each group (4 nibble bytes, 8 sign|mantissa bytes, 16 output
-// bytes; lane-contiguous across a wave).
+// bytes; lane-contiguous across a wave).  A whole tile takes the fast path
+// (no bounds checks); the last, partial tile goes element by element.
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
   constexpr uint32_t kDecTile = kDecTileBf16, kGroups = kDecTile / 2048;
   __shared__ uint32_t bitmap[kDecTile / 32];
   __shared__ alignas(16) uint8_t vals[kDecTile];
+  __shared__ uint32_t tab2[256];
   __shared__ uint32_t s_range[2];
   __shared__ int s_err;
   Header h;
@@ -876,78 +906,65 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
   }
   const uint64_t tile = blockIdx.x;
   const uint64_t chunk = tile / (kChunk / kDecTile);
-  const uint64_t cbi = h.k == 1 ? 0 : (chunk * kChunk) / h.seg;
+  const uint64_t cbi = h.k == 1 ? 0 : codebook_of_chunk(chunk, h.seg / kChunk);
   const uint8_t* cb = a.in + 64 + 16 * cbi;
   const uint32_t tid = threadIdx.x;
   const uint64_t first = tile * kDecTile;
+  const bool fast = first + kDecTile <= a.n;  // same in every thread
+  const uint8_t* nib_t = a.in + h.s.nib + first / 2;
+  const uint8_t* sm_t = a.in + h.s.sm + first;
   // issue the tile's dense loads first: the escape staging overlaps them
   uint32_t nibs[kGroups];
   uint2 sms[kGroups];
+  if (fast) {
 #pragma unroll
-  for (uint32_t g = 0; g < kGroups; ++g) {
-    const uint64_t e0 = first + g * 2048 + 8 * tid;
-    if (e0 + 8 <= a.n) {
-      nibs[g] = ld32(a.in + h.s.nib + e0 / 2);
-      sms[g] = *reinterpret_cast<const uint2*>(a.in + h.s.sm + e0);
+    for (uint32_t g = 0; g < kGroups; ++g) {
+      nibs[g] = ld32(nib_t + g * 1024 + 4 * tid);
+      sms[g] = *reinterpret_cast<const uint2*>(sm_t + g * 2048 + 8 * tid);
     }
   }
-  const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4), l2 = ld32(cb + 8), l3 = ld32(cb + 12);
-  if (!stage_escapes<kDecTile>(a, h, tile, bitmap, vals, s_range, &s_err)) {
+  {  // code-pair table entry tid: codes tid & 15 (even element) and tid >> 4
+    const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4), l2 = ld32(cb + 8), l3 = ld32(cb + 12);
+    const uint32_t c = tid & 0xFFu;
+    const uint32_t pair = lut4((c & 0xFu) | ((c >> 4) << 8), l0, l1, l2, l3);  // bytes 0, 1: the two exponents
+    tab2[c] = ((pair & 0xFFu) << 7) | (((pair >> 8) & 0xFFu) << 23);
+  }
+  if (!stage_escapes<kDecTile>(a, h, tile, bitmap, vals, s_range, &s_err)) {  // its barriers publish tab2
     if (threadIdx.x == 0) report_corrupt(a.status);
     return;
   }
   const uint8_t* bm8 = reinterpret_cast<const uint8_t*>(bitmap);
-  uint16_t* out16 = reinterpret_cast<uint16_t*>(a.out);
+  if (fast) {
+    uint8_t* out_t = a.out + 2 * first;
 #pragma unroll
+    for (uint32_t g = 0; g < kGroups; ++g) {
+      const uint32_t local = g * 2048 + 8 * tid;
+      uint4 o = bf16_decode8(tab2, nibs[g], sms[g]);
+      const uint32_t esc8 = bm8[local >> 3];
+      if (esc8) bf16_patch8(o, esc8, *reinterpret_cast<const uint2*>(vals + local));
+      store_stream(out_t + 2 * local, o);
+    }
+    return;
+  }
+  // last tile: byte-wise loads and stores
+  uint16_t* out16 = reinterpret_cast<uint16_t*>(a.out);
+#pragma unroll 1
   for (uint32_t g = 0; g < kGroups; ++g) {
     const uint32_t local = g * 2048 + 8 * tid;
     const uint64_t e0 = first + local;
     if (e0 >= a.n) break;
     const uint32_t valid = (uint32_t)std::min<uint64_t>(8, a.n - e0);
-    uint32_t nib;
-    uint2 sm;
-    if (valid == 8) {
-      nib = nibs[g];
-      sm = sms[g];
-    } else {
-      uint32_t tn = 0, t0 = 0, t1 = 0;
-      for (uint32_t b = 0; b < (valid + 1) / 2; ++b) tn |= (uint32_t)a.in[h.s.nib + e0 / 2 + b] << (8 * b);
-      for (uint32_t j = 0; j < valid; ++j) {
-        const uint32_t x = (uint32_t)a.in[h.s.sm + e0 + j] << (8 * (j & 3));
-        if (j < 4) t0 |= x;
-        else t1 |= x;
-      }
-      nib = tn;
-      sm = make_uint2(t0, t1);
+    uint32_t tn = 0, t0 = 0, t1 = 0;
+    for (uint32_t b = 0; b < (valid + 1) / 2; ++b) tn |= (uint32_t)nib_t[local / 2 + b] << (8 * b);
+    for (uint32_t j = 0; j < valid; ++j) {
+      const uint32_t x = (uint32_t)sm_t[local + j] << (8 * (j & 3));
+      if (j < 4) t0 |= x;
+      else t1 |= x;
     }
-    uint32_t e_lo = lut4(spread4(nib, 0), l0, l1, l2, l3);
-    uint32_t e_hi = lut4(spread4(nib, 1), l0, l1, l2, l3);
-    // escape overwrite, before the values are assembled: the raw exponents
-    // replace the looked-up bytes where the bitmap is set (vals bytes of
-    // elements without an escape are never used)
-    const uint32_t mask = bm8[local >> 3];
-    if (mask) {
-      const uint2 v = *reinterpret_cast<const uint2*>(vals + local);
-      const uint32_t m_lo = byte_mask4(mask & 0xFu), m_hi = byte_mask4(mask >> 4);
-      e_lo = (e_lo & ~m_lo) | (v.x & m_lo);
-      e_hi = (e_hi & ~m_hi) | (v.y & m_hi);
-    }
-    uint32_t o[4];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint32_t e = half ? e_hi : e_lo;
-      const uint32_t m = half ? sm.y : sm.x;
-      const uint32_t hi = (m & 0x80808080u) | ((e >> 1) & 0x7F7F7F7Fu);
-      const uint32_t lo = ((e << 7) & 0x80808080u) | (m & 0x7F7F7F7Fu);
-      o[2 * half] = perm(hi, lo, 0x05010400u);
-      o[2 * half + 1] = perm(hi, lo, 0x07030602u);
-    }
-    if (valid == 8) {
-      store_stream(out16 + e0, make_uint4(o[0], o[1], o[2], o[3]));
-    } else {
-      for (uint32_t j = 0; j < valid; ++j)
-        out16[e0 + j] = (uint16_t)(pick4(o[0], o[1], o[2], o[3], j >> 1) >> (16 * (j & 1)));
-    }
+    uint4 o = bf16_decode8(tab2, tn, make_uint2(t0, t1));
+    const uint32_t esc8 = bm8[local >> 3];
+    if (esc8) bf16_patch8(o, esc8, *reinterpret_cast<const uint2*>(vals + local));
+    for (uint32_t j = 0; j < valid; ++j) out16[e0 + j] = (uint16_t)(pick4(o.x, o.y, o.z, o.w, j >> 1) >> (16 * (j & 1)));
   }
 }
 
@@ -1014,7 +1031,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
   }
   const uint64_t tile = blockIdx.x;
   const uint64_t chunk = tile / (kChunk / kDecTile);
-  const uint64_t cbi = h.k == 1 ? 0 : (chunk * kChunk) / h.seg;
+  const uint64_t cbi = h.k == 1 ? 0 : codebook_of_chunk(chunk, h.seg / kChunk);
   const uint8_t* cb = a.in + 64 + 16 * cbi;
   const uint32_t tid = threadIdx.x;
   const uint64_t first = tile * kDecTile;
