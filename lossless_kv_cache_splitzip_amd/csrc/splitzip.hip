@@ -11,22 +11,24 @@
 // is stated in include/splitzip.h.
 //
 // GPU design (ours):
-//   prep kernel   header, codebooks, zero padding, clears the scan workspace.
-//   encode        one pass over the input, one cooperative launch of
-//                 co-resident workgroups, each owning a contiguous block of
-//                 8192-element tiles: coalesced 16-byte loads, a 256-entry
-//                 exponent->code table in LDS, nibble and sign|mantissa
-//                 packing with byte-permute ops, coalesced stores.  Escapes
-//                 are ranked in element order with a wave64 DPP scan and an
-//                 LDS block scan and staged in LDS; per-tile counts are
-//                 scanned across workgroups through flagged words, then
-//                 every tile knows its escape base and its records are
-//                 written.
-//   decode        a workgroup owns a 16384-element tile inside one chunk.  It
-//                 binary-searches its slice of the chunk's escape records,
-//                 stages them in LDS (bitmap + values), then rebuilds values
-//                 with the 16-entry LUT held in four registers (v_perm_b32
-//                 lookups) and patches escapes in registers before the store.
+//   prep          header, codebooks and the zero padding between sections.
+//   encode_dense  one workgroup per 8192-element tile: 16-byte loads issued
+//                 before the codebook tables are built in LDS, then codes,
+//                 nibbles and sign|mantissa bytes with byte permutes (E5M2:
+//                 one OR of four per-byte-position table words per input
+//                 word), non-temporal lane-contiguous stores, element-order
+//                 escape ranks (wave64 DPP scan + LDS), escape records staged
+//                 per tile in the workspace.
+//   encode_sums   escape count of each block of 64 tiles.
+//   encode_place  per block: base (sum of lower blocks), tile scan, chunk
+//                 offsets, staged records copied to their place.
+//   decode        one workgroup per tile inside one chunk (8192 BF16 or
+//                 16384 E5M2 elements).  Dense loads go out first; the
+//                 tile's escape records are staged in LDS (bitmap + values),
+//                 from a direct load of a short chunk's records or a 64-way
+//                 wave search of a long one; codes go through an LDS table
+//                 indexed by a whole nibble byte, and escapes are patched in
+//                 registers before non-temporal stores.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -41,8 +43,8 @@ namespace {
 constexpr uint64_t kChunk = 65536;
 constexpr int kThreads = 256;
 constexpr uint64_t kEncTile = 8192;   // elements per encode workgroup
-constexpr uint32_t kDecTileBf16 = 16384;  // elements per decode workgroup
-constexpr uint32_t kDecTileE5m2 = 16384;
+constexpr uint32_t kDecTileBf16 = 8192;   // elements per decode workgroup (measured best: BF16 8192,
+constexpr uint32_t kDecTileE5m2 = 16384;  // E5M2 16384; larger tiles cost occupancy, smaller ones overhead)
 constexpr uint32_t kMagic = 0x00315A53u;
 constexpr uint32_t kMaxK = 65535;
 constexpr uint64_t kMaxN = 1ull << 40;
@@ -806,6 +808,8 @@ __device__ uint64_t wave_lower_bound(const uint8_t* esc, uint64_t lo, uint64_t h
 // the raw exponents.  Every record of the chunk is checked by exactly one of
 // the chunk's tiles (in window, strictly increasing, valid value).  Returns
 // false (the same in every thread) if the stream is invalid.
+constexpr uint32_t kScanRecs = 4;  // records per thread of a chunk staged without a search
+
 template <uint32_t kDecTile>
 __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, uint32_t* bitmap, uint8_t* vals,
                               uint32_t* s_range, int* s_err) {
@@ -822,10 +826,49 @@ __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, 
   if (chunk == 0 && lo != 0) ok = false;
   if (chunk == h.chunks - 1 && hi != h.e) ok = false;
   if (!ok) return false;  // uniform: every thread read the same words
+  const uint32_t vmax = a.dtype == SPLITZIP_BF16 ? 256u : 32u;
+
+  if (hi - lo <= (uint64_t)kScanRecs * kThreads) {  // uniform
+    // short chunk: every tile of the chunk loads all of its records at once
+    // (no search, whose dependent loads would lengthen the tile's critical
+    // path), checks all of them and stages those in its window
+    uint32_t pos[kScanRecs], prev1[kScanRecs], val[kScanRecs];
+#pragma unroll
+    for (uint32_t k = 0; k < kScanRecs; ++k) {
+      const uint64_t r = lo + tid + k * kThreads;
+      pos[k] = ~0u;  // no record
+      if (r < hi) {
+        const uint8_t* rec = a.in + h.s.esc + 3 * r;
+        pos[k] = record_pos(rec);
+        val[k] = rec[2];
+        prev1[k] = r > lo ? record_pos(rec - 3) + 1 : 0;  // predecessor's position + 1, 0 for the first
+      }
+    }
+    for (uint32_t i = tid; i < kDecTile / 32; i += kThreads) bitmap[i] = 0;
+    if (tid == 0) *s_err = 0;
+    __syncthreads();
+    bool bad = false;
+#pragma unroll
+    for (uint32_t k = 0; k < kScanRecs; ++k) {
+      if (pos[k] == ~0u) continue;
+      if (pos[k] >= chunk_len || val[k] >= vmax || prev1[k] > pos[k]) {
+        bad = true;
+        continue;
+      }
+      const uint32_t local = pos[k] - win_lo;  // wraps for pos < win_lo
+      if (local < win_len) {
+        vals[local] = (uint8_t)val[k];
+        atomicOr(&bitmap[local >> 5], 1u << (local & 31));
+      }
+    }
+    if (bad) *s_err = 1;
+    __syncthreads();
+    return *s_err == 0;
+  }
 
   for (uint32_t i = tid; i < kDecTile / 32; i += kThreads) bitmap[i] = 0;
   if (tid == 0) *s_err = 0;
-  // this tile's records: wave 0 finds the first, wave 1 the end
+  // long chunk: wave 0 finds the tile's first record, wave 1 its end
   if (tid < 64) {
     const uint64_t r = q == 0 ? lo : wave_lower_bound(a.in + h.s.esc, lo, hi, win_lo);
     if (tid == 0) s_range[0] = (uint32_t)(r - lo);
@@ -835,7 +878,6 @@ __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, 
   }
   __syncthreads();
   const uint64_t ra = lo + s_range[0], rb = lo + s_range[1];
-  const uint32_t vmax = a.dtype == SPLITZIP_BF16 ? 256u : 32u;
   bool bad = false;
   for (uint64_t r = ra + tid; r < rb; r += kThreads) {
     const uint8_t* rec = a.in + h.s.esc + 3 * r;
@@ -884,7 +926,7 @@ __device__ inline void bf16_patch8(uint4& o, uint32_t esc8, uint2 v) {
   o.w = bf16_patch2(o.w, (esc8 >> 6) & 3u, v.y >> 16);
 }
 
-// BF16 decode tile: 16384 elements = 8 groups of 2048; thread t owns elements
+// BF16 decode tile: 8192 elements = 4 groups of 2048; thread t owns elements
 // 8t..8t+7 of each group (4 nibble bytes, 8 sign|mantissa bytes, 16 output
 // bytes; lane-contiguous across a wave).  A whole tile takes the fast path
 // (no bounds checks); the last, partial tile goes element by element.
