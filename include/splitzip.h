@@ -80,9 +80,10 @@ int splitzip_calibrate(int dtype, const void* host_samples, size_t n_elems, uint
 
 /* Bytes the caller must provide as d_out of splitzip_compress for n_elems
  * elements and n_codebooks codebooks: the largest possible stream (every
- * element escaped) rounded up to 256, plus the encoder's workspace: per 8192-element tile 2052 bytes (a count
- * and a staging slot for up to 512 escape records) and per 64 tiles 8
- * bytes, with 256-byte alignment.  Returns 0 for an invalid dtype,
+ * element escaped) rounded up to 256, plus the encoder's workspace: per
+ * 8192-element tile 2052 bytes (a count and a staging slot for up to 512
+ * escape records), per 64 tiles 8 bytes and per 4096 tiles 8 bytes, with
+ * 256-byte alignment.  Returns 0 for an invalid dtype,
  * n_codebooks == 0 or n_elems > 2^40. */
 size_t splitzip_max_compressed_size(int dtype, size_t n_elems, uint32_t n_codebooks);
 

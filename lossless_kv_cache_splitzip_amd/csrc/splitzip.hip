@@ -85,6 +85,7 @@ __host__ __device__ inline uint64_t workspace_offset(int dtype, uint64_t n, uint
 
 struct Workspace {
   uint64_t* block_sum;
+  uint64_t* super_sum;  // per 64 blocks
   uint32_t* tile_count;
   uint32_t* stage;
   uint64_t end;  // bytes from the stream start
@@ -95,7 +96,8 @@ __host__ inline Workspace workspace_of(uint8_t* out, int dtype, uint64_t n, uint
   Workspace w;
   uint64_t at = workspace_offset(dtype, n, k);
   w.block_sum = reinterpret_cast<uint64_t*>(out + at);
-  at = round256(at + 8 * blocks);
+  w.super_sum = w.block_sum + blocks;
+  at = round256(at + 8 * (blocks + divup(blocks, 64)));
   w.tile_count = reinterpret_cast<uint32_t*>(out + at);  // 16-byte loads in encode_sums
   at = round256(at + 4 * tiles);
   w.stage = reinterpret_cast<uint32_t*>(out + at);
@@ -262,6 +264,7 @@ struct EncArgs {
   uint32_t* tile_count;   // per tile: escapes in it
   uint32_t* stage;        // per tile: kStageSlot records (position | exponent << 16)
   uint64_t* block_sum;    // per block of kBlockTiles tiles: escapes in it
+  uint64_t* super_sum;    // per 64 blocks: escapes in them
   uint64_t* out_bytes;
 };
 
@@ -608,12 +611,15 @@ __device__ void encode_dense(const EncArgs& a) {
 __global__ __launch_bounds__(kThreads) void encode_dense_bf16_kernel(EncArgs a) { encode_dense<true>(a); }
 __global__ __launch_bounds__(kThreads) void encode_dense_e5m2_kernel(EncArgs a) { encode_dense<false>(a); }
 
+// One thread per block of 64 tiles, one wave per 64 blocks (a super-block):
+// block sums, and each wave's total as its super-block sum.
 __global__ __launch_bounds__(kThreads) void encode_sums_kernel(EncArgs a) {
   const uint64_t blk = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (blk >= a.n_blocks) return;
   const uint64_t t0 = blk * kBlockTiles, t1 = std::min<uint64_t>(t0 + kBlockTiles, a.n_tiles);
   uint64_t sum = 0;
-  if (t1 - t0 == kBlockTiles) {  // 16 x 16-byte loads, issued together
+  if (blk >= a.n_blocks) {
+    // past the last block: contributes 0 to its wave's total
+  } else if (t1 - t0 == kBlockTiles) {  // 16 x 16-byte loads, issued together
     const uint4* c = reinterpret_cast<const uint4*>(a.tile_count + t0);
     uint4 v[kBlockTiles / 4];
 #pragma unroll
@@ -623,7 +629,15 @@ __global__ __launch_bounds__(kThreads) void encode_sums_kernel(EncArgs a) {
   } else {
     for (uint64_t t = t0; t < t1; ++t) sum += a.tile_count[t];
   }
-  a.block_sum[blk] = sum;
+  if (blk < a.n_blocks) a.block_sum[blk] = sum;
+  uint64_t v = sum;  // wave total, all 64 lanes active
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
+    v += ((uint64_t)hi << 32) | lo;
+  }
+  if ((threadIdx.x & 63) == 0 && blk < a.n_blocks) a.super_sum[blk >> 6] = v;
 }
 
 constexpr uint32_t kPlaceBatch = 8;  // staged records per thread and step (loads issued together)
@@ -634,9 +648,11 @@ __device__ void encode_place(const EncArgs& a) {
   __shared__ EncShared esh;
   const uint32_t tid = threadIdx.x;
   const uint64_t blk = blockIdx.x;
-  // block base: escapes of all lower blocks
+  // block base: escapes of all lower blocks = the lower super-blocks plus the
+  // lower blocks of this super-block
   uint64_t part = 0;
-  for (uint64_t i = tid; i < blk; i += kThreads) part += a.block_sum[i];
+  for (uint64_t i = tid; i < (blk >> 6); i += kThreads) part += a.super_sum[i];
+  if (tid < (blk & 63)) part += a.block_sum[(blk & ~63ull) + tid];
   {
     // wave sum of u64 through two u32 halves; one lane per wave stores it
     uint64_t v = part;
@@ -1246,6 +1262,7 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
   e.tile_count = w.tile_count;
   e.stage = w.stage;
   e.block_sum = w.block_sum;
+  e.super_sum = w.super_sum;
   e.out_bytes = d_out_bytes;
   const uint32_t tiles = (uint32_t)n_tiles;  // n <= 2^40 -> at most 2^27 tiles
   const uint64_t blocks = divup(n_tiles, kBlockTiles);
