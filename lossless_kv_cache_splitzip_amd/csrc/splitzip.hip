@@ -150,15 +150,6 @@ __device__ inline uint32_t gather4(uint32_t t0, uint32_t t1, uint32_t t2, uint32
   return t0 | (t1 << 8) | (t2 << 16) | (t3 << 24);
 }
 
-// Two words of per-byte codes (elements 0..3 and 4..7) -> 8 nibbles, even
-// element low.
-__device__ inline uint32_t pack_nibbles(uint32_t a, uint32_t b) {
-  uint32_t ca = a & 0x0F0F0F0Fu, cb = b & 0x0F0F0F0Fu;
-  ca |= ca >> 4;  // byte0 = c0 | c1 << 4, byte2 = c2 | c3 << 4
-  cb |= cb >> 4;
-  return perm(cb, ca, 0x06040200u);
-}
-
 // Register-array reads with a run-time index, as selects (no scratch memory).
 __device__ inline uint32_t pick4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t i) {
   return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : a3;
@@ -356,65 +347,78 @@ __device__ inline uint32_t valid_in_group(uint64_t n, uint64_t e0, uint32_t widt
 __device__ inline TileIn load_tile_bf16(const EncArgs& a, uint64_t tile) {
   const uint32_t tid = threadIdx.x;
   const uint64_t first = tile * kEncTile;
-  const uint16_t* in16 = reinterpret_cast<const uint16_t*>(a.in);
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(a.in) + first;
   TileIn in;
   uint4* w = in.w;
+  if (first + kEncTile <= a.n) {  // same in every thread
+#pragma unroll
+    for (int g = 0; g < 4; ++g) w[g] = *reinterpret_cast<const uint4*>(src + g * 2048 + 8 * tid);
+    return in;
+  }
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const uint64_t e0 = first + g * 2048 + 8 * tid;
-    const uint32_t valid = valid_in_group(a.n, e0, 8);
-    if (valid == 8) {
-      w[g] = *reinterpret_cast<const uint4*>(in16 + e0);
-    } else {
-      uint32_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
-      for (uint32_t j = 0; j < valid; ++j) {
-        const uint32_t x = (uint32_t)in16[e0 + j] << (16 * (j & 1));
-        if (j < 2) v0 |= x;
-        else if (j < 4) v1 |= x;
-        else if (j < 6) v2 |= x;
-        else v3 |= x;
-      }
-      w[g] = make_uint4(v0, v1, v2, v3);
+    const uint32_t local = g * 2048 + 8 * tid;
+    const uint32_t valid = valid_in_group(a.n, first + local, 8);
+    uint32_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
+    for (uint32_t j = 0; j < valid; ++j) {
+      const uint32_t x = (uint32_t)src[local + j] << (16 * (j & 1));
+      if (j < 2) v0 |= x;
+      else if (j < 4) v1 |= x;
+      else if (j < 6) v2 |= x;
+      else v3 |= x;
     }
+    w[g] = make_uint4(v0, v1, v2, v3);
   }
   return in;
+}
+
+// Codes of one word of four table entries (code | escape << 4 per byte) and
+// the next word, as 8 nibbles (even element low): per byte, the code and the
+// next byte's code moved to the high nibble, then the even bytes.
+__device__ inline uint32_t pack_codes8(uint32_t c_lo, uint32_t c_hi) {
+  const uint32_t u = (c_lo & 0x0F0F0F0Fu) | ((c_lo >> 4) & 0xF0F0F0F0u);
+  const uint32_t v = (c_hi & 0x0F0F0F0Fu) | ((c_hi >> 4) & 0xF0F0F0F0u);
+  return perm(v, u, 0x06040200u);
 }
 
 __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store) {
   const uint32_t tid = threadIdx.x;
   const uint64_t first = tile * kEncTile;
+  const bool tile_full = first + kEncTile <= a.n;  // same in every thread
   const uint4* w = in.w;
-  uint32_t valid[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) valid[g] = valid_in_group(a.n, first + g * 2048 + 8 * tid, 8);
   TileEsc r;
   uint32_t cnt[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
+    const uint32_t local = g * 2048 + 8 * tid;
     const uint4 x = w[g];
     const uint8_t* tb = sh.table;
     uint32_t lo = gather4(tb[(x.x >> 7) & 0xFF], tb[(x.x >> 23) & 0xFF], tb[(x.y >> 7) & 0xFF], tb[(x.y >> 23) & 0xFF]);
     uint32_t hi = gather4(tb[(x.z >> 7) & 0xFF], tb[(x.z >> 23) & 0xFF], tb[(x.w >> 7) & 0xFF], tb[(x.w >> 23) & 0xFF]);
-    if (valid[g] < 8) {
-      lo &= keep_low_bytes(valid[g]);
-      hi &= valid[g] > 4 ? keep_low_bytes(valid[g] - 4) : 0u;
+    uint32_t valid = 8;
+    if (!tile_full) {  // elements past n: no code, no escape
+      valid = valid_in_group(a.n, first + local, 8);
+      lo &= keep_low_bytes(valid);
+      hi &= valid > 4 ? keep_low_bytes(valid - 4) : 0u;
     }
-    r.mask[g] = flag_mask4(lo) | (flag_mask4(hi) << 4);
-    cnt[g] = __builtin_popcount(r.mask[g]);
+    // escape flags, element k of lo at bit 8k and element 4 + k at bit 8k + 1
+    const uint32_t f = ((lo >> 4) & 0x01010101u) | ((hi >> 3) & 0x02020202u);
+    r.mask[g] = f;
+    cnt[g] = __builtin_popcount(f);
     if (store) {
-      const uint32_t nib = pack_nibbles(lo, hi);
+      const uint32_t nib = pack_codes8(lo, hi);
       // sign|mantissa: high bytes and low bytes of the four BF16 pairs
       const uint32_t h01 = perm(x.y, x.x, 0x07050301u), l01 = perm(x.y, x.x, 0x06040200u);
       const uint32_t h23 = perm(x.w, x.z, 0x07050301u), l23 = perm(x.w, x.z, 0x06040200u);
       const uint32_t sm0 = (h01 & 0x80808080u) | (l01 & 0x7F7F7F7Fu);
       const uint32_t sm1 = (h23 & 0x80808080u) | (l23 & 0x7F7F7F7Fu);
-      const uint64_t e0 = first + g * 2048 + 8 * tid;
-      if (valid[g] == 8) {
-        store_stream(a.out + a.nib + e0 / 2, nib);
-        store_stream(a.out + a.sm + e0, make_uint2(sm0, sm1));
-      } else if (valid[g] > 0) {
-        for (uint32_t b = 0; b < (valid[g] + 1) / 2; ++b) a.out[a.nib + e0 / 2 + b] = (uint8_t)(nib >> (8 * b));
-        for (uint32_t j = 0; j < valid[g]; ++j) a.out[a.sm + e0 + j] = (uint8_t)((j < 4 ? sm0 : sm1) >> (8 * (j & 3)));
+      if (tile_full) {
+        store_stream(a.out + a.nib + first / 2 + local / 2, nib);
+        store_stream(a.out + a.sm + first + local, make_uint2(sm0, sm1));
+      } else if (valid > 0) {
+        const uint64_t e0 = first + local;
+        for (uint32_t b = 0; b < (valid + 1) / 2; ++b) a.out[a.nib + e0 / 2 + b] = (uint8_t)(nib >> (8 * b));
+        for (uint32_t j = 0; j < valid; ++j) a.out[a.sm + e0 + j] = (uint8_t)((j < 4 ? sm0 : sm1) >> (8 * (j & 3)));
       }
     }
   }
@@ -452,7 +456,8 @@ __device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, con
   const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTile;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    uint32_t m = r.mask[g];
+    const uint32_t f = r.mask[g];  // element k at bit 8k, element 4 + k at bit 8k + 1
+    uint32_t m = f ? flag_mask4(f << 4) | (flag_mask4(f << 3) << 4) : 0u;  // element order
     uint32_t k = r.rank[g];
     const uint64_t e0 = tile * kEncTile + g * 2048 + 8 * tid;
     while (m) {
