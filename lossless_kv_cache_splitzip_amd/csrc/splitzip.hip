@@ -12,9 +12,10 @@
 //
 // GPU design (ours):
 //   prep          header, codebooks and the zero padding between sections.
-//   encode_dense  one workgroup per 8192-element tile: 16-byte loads issued
-//                 before the codebook tables are built in LDS, then codes,
-//                 nibbles and sign|mantissa bytes with byte permutes (E5M2:
+//   encode_dense  one workgroup per tile (8192 BF16 or 16384 E5M2 elements):
+//                 16-byte loads issued before the codebook tables are built
+//                 in LDS, then codes, nibbles and sign|mantissa bytes with
+//                 byte permutes (E5M2:
 //                 one OR of four per-byte-position table words per input
 //                 word), non-temporal lane-contiguous stores, element-order
 //                 escape ranks (wave64 DPP scan + LDS), escape records staged
@@ -42,7 +43,8 @@ namespace {
 
 constexpr uint64_t kChunk = 65536;
 constexpr int kThreads = 256;
-constexpr uint64_t kEncTile = 8192;   // elements per encode workgroup
+constexpr uint64_t kEncTileBf16 = 8192;   // elements per encode workgroup
+constexpr uint64_t kEncTileE5m2 = 16384;
 constexpr uint32_t kDecTileBf16 = 8192;   // elements per decode workgroup (measured best: BF16 8192,
 constexpr uint32_t kDecTileE5m2 = 16384;  // E5M2 16384; larger tiles cost occupancy, smaller ones overhead)
 constexpr uint32_t kMagic = 0x00315A53u;
@@ -320,7 +322,7 @@ __device__ inline void build_table(const EncArgs& a, EncShared& sh, uint64_t cbi
 // thread's first escape in each group, and the escape masks.
 struct TileEsc {
   uint32_t agg;      // escapes in the tile
-  uint32_t rank[4];  // BF16: per group of 8 (4 groups); E5M2: per group of 16 (2 groups)
+  uint32_t rank[4];  // per group (4 groups: BF16 8 elements per thread, E5M2 16)
   uint32_t mask[4];  // escaped elements of each group, bit j = element j
 };
 
@@ -331,6 +333,32 @@ __device__ inline void wave_totals_to_lds(EncShared& sh, uint32_t i01, uint32_t 
     sh.wave[4 + wave] = i23;
   }
   __syncthreads();
+}
+
+// Element-order ranks of a tile of four groups: groups are ordered (g,
+// thread), so the four per-thread counts are scanned as 16-bit fields (a
+// group holds at most 4096 escapes).
+__device__ inline void tile_ranks4(EncShared& sh, const uint32_t cnt[4], TileEsc& r) {
+  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t p01 = cnt[0] | (cnt[1] << 16), p23 = cnt[2] | (cnt[3] << 16);
+  const uint32_t i01 = wave_inclusive_sum(p01), i23 = wave_inclusive_sum(p23);
+  wave_totals_to_lds(sh, i01, i23);
+  uint32_t pre01 = 0, pre23 = 0, tot01 = 0, tot23 = 0;
+#pragma unroll
+  for (uint32_t v = 0; v < 4; ++v) {
+    const uint32_t x = sh.wave[v], y = sh.wave[4 + v];
+    pre01 += v < wave ? x : 0u;
+    pre23 += v < wave ? y : 0u;
+    tot01 += x;
+    tot23 += y;
+  }
+  const uint32_t g0 = tot01 & 0xFFFF, g1 = tot01 >> 16, g2 = tot23 & 0xFFFF, g3 = tot23 >> 16;
+  r.agg = g0 + g1 + g2 + g3;
+  const uint32_t x01 = pre01 + i01 - p01, x23 = pre23 + i23 - p23;
+  r.rank[0] = x01 & 0xFFFF;
+  r.rank[1] = g0 + (x01 >> 16);
+  r.rank[2] = g0 + g1 + (x23 & 0xFFFF);
+  r.rank[3] = g0 + g1 + g2 + (x23 >> 16);
 }
 
 // BF16 tile: 8192 elements = 4 groups of 2048; thread t owns elements
@@ -346,11 +374,11 @@ __device__ inline uint32_t valid_in_group(uint64_t n, uint64_t e0, uint32_t widt
 
 __device__ inline TileIn load_tile_bf16(const EncArgs& a, uint64_t tile) {
   const uint32_t tid = threadIdx.x;
-  const uint64_t first = tile * kEncTile;
+  const uint64_t first = tile * kEncTileBf16;
   const uint16_t* src = reinterpret_cast<const uint16_t*>(a.in) + first;
   TileIn in;
   uint4* w = in.w;
-  if (first + kEncTile <= a.n) {  // same in every thread
+  if (first + kEncTileBf16 <= a.n) {  // same in every thread
 #pragma unroll
     for (int g = 0; g < 4; ++g) w[g] = *reinterpret_cast<const uint4*>(src + g * 2048 + 8 * tid);
     return in;
@@ -383,8 +411,8 @@ __device__ inline uint32_t pack_codes8(uint32_t c_lo, uint32_t c_hi) {
 
 __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store) {
   const uint32_t tid = threadIdx.x;
-  const uint64_t first = tile * kEncTile;
-  const bool tile_full = first + kEncTile <= a.n;  // same in every thread
+  const uint64_t first = tile * kEncTileBf16;
+  const bool tile_full = first + kEncTileBf16 <= a.n;  // same in every thread
   const uint4* w = in.w;
   TileEsc r;
   uint32_t cnt[4];
@@ -422,28 +450,7 @@ __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t ti
       }
     }
   }
-  // element-order ranks: groups are ordered (g, thread), so scan the four
-  // per-thread counts as 16-bit fields (a group holds at most 2048 escapes)
-  const uint32_t p01 = cnt[0] | (cnt[1] << 16), p23 = cnt[2] | (cnt[3] << 16);
-  const uint32_t i01 = wave_inclusive_sum(p01), i23 = wave_inclusive_sum(p23);
-  wave_totals_to_lds(sh, i01, i23);
-  const uint32_t wave = tid >> 6;
-  uint32_t pre01 = 0, pre23 = 0, tot01 = 0, tot23 = 0;
-#pragma unroll
-  for (uint32_t v = 0; v < 4; ++v) {
-    const uint32_t x = sh.wave[v], y = sh.wave[4 + v];
-    pre01 += v < wave ? x : 0u;
-    pre23 += v < wave ? y : 0u;
-    tot01 += x;
-    tot23 += y;
-  }
-  const uint32_t g0 = tot01 & 0xFFFF, g1 = tot01 >> 16, g2 = tot23 & 0xFFFF, g3 = tot23 >> 16;
-  r.agg = g0 + g1 + g2 + g3;
-  const uint32_t x01 = pre01 + i01 - p01, x23 = pre23 + i23 - p23;
-  r.rank[0] = x01 & 0xFFFF;
-  r.rank[1] = g0 + (x01 >> 16);
-  r.rank[2] = g0 + g1 + (x23 & 0xFFFF);
-  r.rank[3] = g0 + g1 + g2 + (x23 >> 16);
+  tile_ranks4(sh, cnt, r);
   return r;
 }
 
@@ -453,13 +460,13 @@ template <typename Put>
 __device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put) {
   const uint32_t tid = threadIdx.x;
   const uint16_t* in16 = reinterpret_cast<const uint16_t*>(a.in);
-  const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTile;
+  const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTileBf16;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const uint32_t f = r.mask[g];  // element k at bit 8k, element 4 + k at bit 8k + 1
     uint32_t m = f ? flag_mask4(f << 4) | (flag_mask4(f << 3) << 4) : 0u;  // element order
     uint32_t k = r.rank[g];
-    const uint64_t e0 = tile * kEncTile + g * 2048 + 8 * tid;
+    const uint64_t e0 = tile * kEncTileBf16 + g * 2048 + 8 * tid;
     while (m) {
       const uint32_t j = __builtin_ctz(m);
       m &= m - 1;
@@ -468,21 +475,21 @@ __device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, con
   }
 }
 
-// E5M2 tile: 8192 elements = 2 groups of 4096; thread t owns elements
+// E5M2 tile: 16384 elements = 4 groups of 4096; thread t owns elements
 // 16t..16t+15 of each group: 16 input bytes, 8 nibble bytes and 6
 // sign|mantissa bytes, all lane-contiguous across a wave.
 __device__ inline TileIn load_tile_e5m2(const EncArgs& a, uint64_t tile) {
   TileIn in;
   const uint32_t tid = threadIdx.x;
-  const uint64_t first = tile * kEncTile;
+  const uint64_t first = tile * kEncTileE5m2;
   const uint8_t* src = a.in + first;
-  if (first + kEncTile <= a.n) {  // same in every thread
+  if (first + kEncTileE5m2 <= a.n) {  // same in every thread
 #pragma unroll
-    for (int g = 0; g < 2; ++g) in.w[g] = *reinterpret_cast<const uint4*>(src + g * 4096 + 16 * tid);
+    for (int g = 0; g < 4; ++g) in.w[g] = *reinterpret_cast<const uint4*>(src + g * 4096 + 16 * tid);
     return in;
   }
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
+  for (int g = 0; g < 4; ++g) {
     const uint32_t local = g * 4096 + 16 * tid;
     const uint32_t valid = valid_in_group(a.n, first + local, 16);
     uint32_t v[4] = {0, 0, 0, 0};
@@ -503,12 +510,12 @@ __device__ inline uint32_t e5m2_pos_word(const uint32_t* pos4, uint32_t x) {
 
 __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store) {
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint64_t first = tile * kEncTile;
-  const bool tile_full = first + kEncTile <= a.n;  // same in every thread
+  const uint64_t first = tile * kEncTileE5m2;
+  const bool tile_full = first + kEncTileE5m2 <= a.n;  // same in every thread
   TileEsc r;
-  uint32_t cnt[2];
+  uint32_t cnt[4];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
+  for (int g = 0; g < 4; ++g) {
     const uint32_t local = g * 4096 + 16 * tid;
     const uint32_t r0 = e5m2_pos_word(sh.pos4, in.w[g].x), r1 = e5m2_pos_word(sh.pos4, in.w[g].y);
     const uint32_t r2 = e5m2_pos_word(sh.pos4, in.w[g].z), r3 = e5m2_pos_word(sh.pos4, in.w[g].w);
@@ -554,33 +561,19 @@ __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t ti
         a.out[smo + b] = (uint8_t)((b < 4 ? lo : hi) >> (8 * (b & 3)));
     }
   }
-  // element-order ranks: groups are ordered (g, thread); two 16-bit fields
-  const uint32_t p = cnt[0] | (cnt[1] << 16);
-  const uint32_t inc = wave_inclusive_sum(p);
-  wave_totals_to_lds(sh, inc, 0);
-  uint32_t pre = 0, tot = 0;
-#pragma unroll
-  for (uint32_t v = 0; v < 4; ++v) {
-    pre += v < wave ? sh.wave[v] : 0u;
-    tot += sh.wave[v];
-  }
-  const uint32_t g0 = tot & 0xFFFF, g1 = tot >> 16;
-  const uint32_t x = pre + inc - p;
-  r.agg = g0 + g1;
-  r.rank[0] = x & 0xFFFF;
-  r.rank[1] = g0 + (x >> 16);
+  tile_ranks4(sh, cnt, r);
   return r;
 }
 
 template <typename Put>
 __device__ inline void for_each_escape_e5m2(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put) {
   const uint32_t tid = threadIdx.x;
-  const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTile;
+  const uint32_t in_chunk = (uint32_t)(tile & 3) * (uint32_t)kEncTileE5m2;
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
+  for (int g = 0; g < 4; ++g) {
     uint32_t m = r.mask[g];
     uint32_t k = r.rank[g];
-    const uint64_t e0 = tile * kEncTile + g * 4096 + 16 * tid;
+    const uint64_t e0 = tile * kEncTileE5m2 + g * 4096 + 16 * tid;
     while (m) {
       const uint32_t j = __builtin_ctz(m);
       m &= m - 1;
@@ -602,7 +595,7 @@ __device__ void encode_dense(const EncArgs& a) {
   __shared__ EncShared sh;
   const uint64_t t = blockIdx.x;
   const TileIn in = kBf16 ? load_tile_bf16(a, t) : load_tile_e5m2(a, t);  // in flight during the table build
-  build_table(a, sh, a.seg_chunks ? codebook_of_chunk(t >> 3, a.seg_chunks) : 0, kBf16 ? 256u : 32u);
+  build_table(a, sh, a.seg_chunks ? codebook_of_chunk(t >> (kBf16 ? 3 : 2), a.seg_chunks) : 0, kBf16 ? 256u : 32u);
   const TileEsc r = kBf16 ? encode_tile_bf16(a, sh, t, in, true) : encode_tile_e5m2(a, sh, t, in, true);
   if (threadIdx.x == 0) a.tile_count[t] = r.agg;
   if (r.agg <= kStageSlot) {
@@ -688,7 +681,8 @@ __device__ void encode_place(const EncArgs& a) {
   if (tid == 0) sh.overflow = 0;
   __syncthreads();
   if (mine) {
-    if ((t & 7) == 0) put_le(a.out + a.offsets + 8 * (t >> 3), base + pre, 8);
+    constexpr uint32_t kTpcLog2 = kBf16 ? 3 : 2;  // tiles per chunk: 8 BF16, 4 E5M2
+    if ((t & ((1u << kTpcLog2) - 1)) == 0) put_le(a.out + a.offsets + 8 * (t >> kTpcLog2), base + pre, 8);
     if (!staged) atomicOr(&sh.overflow, 1u);
     if (t == a.n_tiles - 1) {
       const uint64_t e = std::min<uint64_t>(base + pre + cnt, a.n);
@@ -735,7 +729,7 @@ __device__ void encode_place(const EncArgs& a) {
     const uint32_t n_i = sh.pre_all[i + 1] - sh.pre_all[i];
     if (n_i <= kStageSlot) continue;  // uniform
     const uint64_t tt = blk * kBlockTiles + i;
-    const uint64_t cbi = a.seg_chunks ? codebook_of_chunk(tt >> 3, a.seg_chunks) : 0;
+    const uint64_t cbi = a.seg_chunks ? codebook_of_chunk(tt >> (kBf16 ? 3 : 2), a.seg_chunks) : 0;
     if (cbi != table_cb) {
       build_table(a, esh, cbi, kBf16 ? 256u : 32u);
       table_cb = cbi;
@@ -1224,7 +1218,7 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
 
   const uint64_t n = n_elems;
   const Sections s = sections_of(dtype, n, n_codebooks);
-  const uint64_t n_tiles = divup(n, kEncTile);
+  const uint64_t n_tiles = divup(n, dtype == SPLITZIP_BF16 ? kEncTileBf16 : kEncTileE5m2);
   uint8_t* out = static_cast<uint8_t*>(d_out);
   const Workspace w = workspace_of(out, dtype, n, n_codebooks);
 
