@@ -15,13 +15,12 @@
 //   encode_dense  one workgroup per tile (8192 BF16 or 16384 E5M2 elements):
 //                 16-byte loads issued before the codebook tables are built
 //                 in LDS, then codes, nibbles and sign|mantissa bytes with
-//                 byte permutes (E5M2:
-//                 one OR of four per-byte-position table words per input
-//                 word), non-temporal lane-contiguous stores, element-order
-//                 escape ranks (wave64 DPP scan + LDS), escape records staged
-//                 per tile in the workspace.
+//                 byte permutes (E5M2: one OR of four per-byte-position
+//                 table words per input word), non-temporal lane-contiguous
+//                 stores, element-order escape ranks (wave64 DPP scan +
+//                 LDS), escape records staged per tile in the workspace.
 //   encode_sums   escape count of each block of 64 tiles.
-//   encode_place  per block: base (sum of lower blocks), tile scan, chunk
+//   encode_place  per block: base (lower super-blocks and blocks), tile scan, chunk
 //                 offsets, staged records copied to their place.
 //   decode        one workgroup per tile inside one chunk (8192 BF16 or
 //                 16384 E5M2 elements).  Dense loads go out first; the
