@@ -267,12 +267,15 @@ constexpr uint32_t kBlockTiles = 64;  // tiles per encode_place workgroup
 struct EncShared {
   uint8_t table[256];
   // E5M2: word for input byte b at byte position j of a 4-element word:
-  // code << 4j | (sign << 2 | mantissa) << (16 + 3j) | escaped << (28 + j)
+  // code << 4j | (sign << 2 | mantissa) << (16 + 3j) | escaped << (28 + j).
+  // After the tile's rank scan it holds the tile's staged escape records.
   uint32_t pos4[4 * 256];
   uint32_t wave[8];
   uint64_t red[16];
   alignas(16) uint32_t s3[4 * 96];  // E5M2: a wave's 64 x 6 sign|mantissa bytes, gathered for aligned stores
 };
+
+static_assert(kStageSlot <= 4 * 256, "staged records reuse the E5M2 table space");
 
 struct PlaceShared {
   uint64_t red[16];
@@ -597,11 +600,17 @@ __device__ void encode_dense(const EncArgs& a) {
   build_table(a, sh, a.seg_chunks ? codebook_of_chunk(t >> (kBf16 ? 3 : 2), a.seg_chunks) : 0, kBf16 ? 256u : 32u);
   const TileEsc r = kBf16 ? encode_tile_bf16(a, sh, t, in, true) : encode_tile_e5m2(a, sh, t, in, true);
   if (threadIdx.x == 0) a.tile_count[t] = r.agg;
-  if (r.agg <= kStageSlot) {
-    uint32_t* slot = a.stage + t * kStageSlot;
-    auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) { slot[k] = pos | (val << 16); };
+  if (r.agg <= kStageSlot) {  // uniform
+    // records gathered in LDS first (the E5M2 tables are dead after the
+    // rank scan's barrier), then written to the slot with contiguous
+    // stores instead of scattered 4-byte ones
+    uint32_t* rec = sh.pos4;
+    auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) { rec[k] = pos | (val << 16); };
     if (kBf16) for_each_escape_bf16(a, t, r, stage);
     else for_each_escape_e5m2(a, t, r, stage);
+    __syncthreads();
+    uint32_t* slot = a.stage + t * kStageSlot;
+    for (uint32_t i = threadIdx.x; i < r.agg; i += kThreads) slot[i] = rec[i];
   }
 }
 
