@@ -122,6 +122,69 @@ def cpu_baseline(wl_name: str, budget_s: float, threads: int):
     return serial, parallel
 
 
+def link_leg(wl, cbs, seg, dtype, reps: int = 3):
+    """The pages' transfer setting on one GPU: the workload moves through
+    pinned host memory over PCIe in groups of 16 MiB of raw data, up to
+    4 groups in flight, once raw and once compressed (compress -> copy to
+    host -> copy back -> decompress, copies by the copy engines).  Wall time of the blocking
+    pipelined call, best of `reps` after one warm-up each.  As context, the
+    copy engines moving the whole tensor to host and back at once."""
+    import torch
+
+    import lossless_kv_cache_splitzip_amd as sz
+
+    elem = wl.data.element_size()
+    group = (16 << 20) // elem
+    if seg and seg % group and group % seg:
+        group = seg
+    p = sz.Pipeline(dtype, wl.n, cbs, seg, group, 4, device=wl.data.device)
+    out = torch.empty_like(wl.data)
+    status = torch.zeros(1, dtype=torch.int32, device=wl.data.device)
+    res = {}
+    for mode in ("raw", "compressed"):
+        best, sent = float("inf"), 0
+        for r in range(reps + 1):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            sizes = p.transfer(wl.data, out, compress=(mode == "compressed"), status=status)
+            t1 = time.perf_counter()
+            if r:
+                best = min(best, t1 - t0)
+            sent = int(sizes.sum())
+        assert int(status.item()) == 0 and torch.equal(out.view(torch.uint8), wl.data.view(torch.uint8))
+        res[mode] = (best * 1e3, sent)
+    del p
+    # copy engines: the whole tensor to pinned host memory, and a second
+    # pinned buffer to the device, concurrently (both link directions)
+    src = wl.data.view(torch.uint8)
+    h1 = torch.empty(src.numel(), dtype=torch.uint8, pin_memory=True)
+    h2 = torch.empty(src.numel(), dtype=torch.uint8, pin_memory=True)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    dma = float("inf")
+    for r in range(reps + 1):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s1):
+            h1.copy_(src, non_blocking=True)
+        with torch.cuda.stream(s2):
+            out.view(torch.uint8).copy_(h2, non_blocking=True)
+        torch.cuda.synchronize()
+        if r:
+            dma = min(dma, time.perf_counter() - t0)
+    del h1, h2, out
+    raw_ms, raw_sent = res["raw"]
+    c_ms, c_sent = res["compressed"]
+    return {
+        "link": "pinned host memory over PCIe, copy engines both ways",
+        "group_elems": group, "depth": 4,
+        "raw_ms": raw_ms, "compressed_ms": c_ms, "speedup": raw_ms / c_ms,
+        "raw_bytes": raw_sent, "compressed_bytes": c_sent,
+        "raw_GBps": wl.raw_bytes / (raw_ms / 1e3) / 1e9,
+        "compressed_GBps": wl.raw_bytes / (c_ms / 1e3) / 1e9,
+        "copy_engines_both_ways_ms": dma * 1e3,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +194,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1),
                     help="host threads of the parallel oracle run (the box grants 16)")
+    ap.add_argument("--no-link", action="store_true", help="skip the pipelined host-link transfer leg")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this codec benchmark runs on one GPU; multi-GPU runs are not part of it",
@@ -218,6 +282,10 @@ def main():
     sfx = "bf16" if dtype == kvsynth.BF16 else "e5m2"
     enc_kernels = ["prep_kernel", f"encode_dense_{sfx}_kernel", "encode_sums_kernel", f"encode_place_{sfx}_kernel"]
     dname = f"decode_{sfx}_kernel"
+    link = None if args.no_link else link_leg(wl, cbs, seg, dtype)
+    if link:
+        log(f"[bench] link: raw {link['raw_ms']:.2f} ms, compressed {link['compressed_ms']:.2f} ms, "
+            f"speedup {link['speedup']:.3f}")
     cpu, cpu_par = cpu_baseline(args.workload, args.cpu_budget, args.cpu_threads) if args.cpu_budget > 0 else (None, None)
 
     line = {
@@ -255,6 +323,7 @@ def main():
                             "frac_of_memcpy": enc_gbps / copy_gbps,
                             "traffic": counter_traffic(enc_kernels, args.workload), "algorithmic_bytes": alg_enc},
         "cpu_baseline": cpu,
+        "link_transfer": link,
         "cpu_baseline_parallel": cpu_par,
         "pages_context": {"encode_GBps": 613.3, "decode_GBps": 2181.8, "hardware": "not stated in the pages"},
         "kernel_source_sha256_16": source_digest(),

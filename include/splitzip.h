@@ -131,6 +131,53 @@ int splitzip_decompress(const void* d_in, size_t in_bytes, int dtype, size_t n_e
 /* Static text for a status code. */
 const char* splitzip_status_string(int status);
 
+/* ---- Chunk-pipelined transfer through a host link -------------------------
+ * The pages' setting is a KV cache moving from a prefill node to a decode
+ * node over a 50-100 GB/s link, where the codec shrinks the transferred bytes
+ * and pays for itself (technical summary, "Planteamiento del Problema" and
+ * "Resultados": 1.22-1.32x faster transfers).  On one GPU the link is the
+ * PCIe path to pinned host memory: each group of group_elems elements is
+ * compressed (splitzip_compress), copied to host memory and back by the copy
+ * engines, and decompressed (splitzip_decompress) into d_out, with up to
+ * `depth` groups in flight.  A compressed group's size exists only on the
+ * device: the encoder writes it into the link buffer, and the host, one group
+ * behind the encoder, polls it before queuing that group's copies.
+ *
+ * Each group is a complete SZ1 stream of its own elements.  group_elems is a
+ * non-zero multiple of 65536; with n_codebooks > 1, group_elems is a multiple
+ * of segment_elems or divides it, so a group uses the codebooks of the
+ * segments it covers.  depth is 2..32.
+ *
+ * splitzip_pipeline_sizes: bytes of the device work area (2 * depth slots)
+ * and of the pinned host link buffer (depth slots, then one u64 per group:
+ * the bytes it sent).  Returns SPLITZIP_OK or SPLITZIP_E_INVALID. */
+int splitzip_pipeline_sizes(int dtype, size_t n_elems, uint32_t n_codebooks, size_t segment_elems,
+                            size_t group_elems, uint32_t depth, size_t* d_work_bytes, size_t* h_link_bytes);
+
+/* splitzip_pipeline_transfer: d_in (n_elems, device, 16-byte aligned) ->
+ * d_out (device, 16-byte aligned).
+ *   compress      1: groups travel compressed; 0: the raw groups travel the
+ *                 same pipeline (the uncompressed baseline).
+ *   d_work        device memory of d_work_bytes, 256-byte aligned.
+ *   h_link        pinned host memory (hipHostMalloc with hipHostMallocCoherent,
+ *                 so the encoder's size words reach the host at once) of
+ *                 h_link_bytes, 256-byte aligned.
+ *   d_status      optional device int32, as in splitzip_decompress.
+ *   h_group_bytes optional host array of ceil(n / group_elems) entries: the
+ *                 bytes each group sent over the link.
+ *   streams       four distinct streams: encode, device-to-host copies,
+ *                 host-to-device copies, decode.
+ * Blocking: the calling thread drives the pipeline and returns after all four
+ * streams are synchronized.  On an error return, work already queued may
+ * still run; synchronize the streams before reusing the buffers.  Returns
+ * SPLITZIP_OK, SPLITZIP_E_INVALID, SPLITZIP_E_CAPACITY, SPLITZIP_E_CODEBOOK
+ * or SPLITZIP_E_HIP. */
+int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks,
+                               uint32_t n_codebooks, size_t segment_elems, size_t group_elems, uint32_t depth,
+                               int compress, void* d_work, size_t d_work_bytes, void* h_link, size_t h_link_bytes,
+                               void* d_out, int32_t* d_status, uint64_t* h_group_bytes,
+                               const hipStream_t streams[4]);
+
 #ifdef __cplusplus
 }
 #endif

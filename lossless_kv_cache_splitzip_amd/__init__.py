@@ -16,6 +16,7 @@ from ._native import (  # noqa: F401
     FP8_E5M2,
     LIB_PATH,
     OK,
+    Pipeline,
     SplitZipError,
     compress,
     decompress,
@@ -24,5 +25,7 @@ from ._native import (  # noqa: F401
     splitzip_compress,
     splitzip_decompress,
     splitzip_max_compressed_size,
+    splitzip_pipeline_sizes,
+    splitzip_pipeline_transfer,
     status_string,
 )

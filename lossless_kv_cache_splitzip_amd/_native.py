@@ -29,6 +29,8 @@ EXPORTS = (
     "splitzip_compress",
     "splitzip_decompress",
     "splitzip_status_string",
+    "splitzip_pipeline_sizes",
+    "splitzip_pipeline_transfer",
 )
 
 _lib = None
@@ -62,6 +64,10 @@ def load():
     lib.splitzip_decompress.restype = i32
     lib.splitzip_status_string.argtypes = [i32]
     lib.splitzip_status_string.restype = ctypes.c_char_p
+    lib.splitzip_pipeline_sizes.argtypes = [i32, sz, u32, sz, sz, u32, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.splitzip_pipeline_sizes.restype = i32
+    lib.splitzip_pipeline_transfer.argtypes = [i32, vp, sz, vp, u32, sz, sz, u32, i32, vp, sz, vp, sz, vp, vp, vp, vp]
+    lib.splitzip_pipeline_transfer.restype = i32
     _lib = lib
     return lib
 
@@ -98,6 +104,30 @@ def splitzip_decompress(d_in: int, in_bytes: int, dtype: int, n_elems: int, d_ou
                         d_status: int | None, stream: int | None) -> int:
     return int(load().splitzip_decompress(d_in or None, in_bytes, dtype, n_elems, d_out or None,
                                           d_status or None, stream or None))
+
+
+def splitzip_pipeline_sizes(dtype: int, n_elems: int, n_codebooks: int, segment_elems: int, group_elems: int,
+                            depth: int) -> tuple[int, int]:
+    """(device work bytes, pinned host link bytes) of a pipelined transfer."""
+    d, h = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    rc = load().splitzip_pipeline_sizes(dtype, n_elems, n_codebooks, segment_elems, group_elems, depth,
+                                        ctypes.byref(d), ctypes.byref(h))
+    if rc != OK:
+        raise SplitZipError(rc, "splitzip_pipeline_sizes")
+    return int(d.value), int(h.value)
+
+
+def splitzip_pipeline_transfer(dtype: int, d_in: int, n_elems: int, h_codebooks: np.ndarray, n_codebooks: int,
+                               segment_elems: int, group_elems: int, depth: int, compress: bool, d_work: int,
+                               work_bytes: int, h_link: int, link_bytes: int, d_out: int, d_status: int | None,
+                               h_group_bytes: np.ndarray | None, streams) -> int:
+    cbs = np.ascontiguousarray(h_codebooks, dtype=np.uint8)
+    arr = (ctypes.c_void_p * 4)(*[int(s) for s in streams])
+    gb = None if h_group_bytes is None else h_group_bytes.ctypes.data
+    return int(load().splitzip_pipeline_transfer(dtype, d_in or None, n_elems, cbs.ctypes.data, n_codebooks,
+                                                 segment_elems, group_elems, depth, int(bool(compress)),
+                                                 d_work or None, work_bytes, h_link or None, link_bytes,
+                                                 d_out or None, d_status or None, gb, arr))
 
 
 # -------------------------------------------------------- torch conveniences
@@ -176,3 +206,79 @@ def decompress(stream_buf, n_elems: int, dtype: int, out=None, status=None, in_b
     if rc != OK:
         raise SplitZipError(rc, "splitzip_decompress")
     return out, status
+
+
+_hip = None
+
+
+def _hip_runtime():
+    """The HIP runtime, for the coherent pinned host buffer of the link."""
+    global _hip
+    if _hip is None:
+        import torch  # noqa: F401  (loads the runtime torch was built with)
+        for name in ("libamdhip64.so", "libamdhip64.so.7", "libamdhip64.so.6", "/opt/rocm/lib/libamdhip64.so"):
+            try:
+                _hip = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if _hip is None:
+            raise RuntimeError("libamdhip64 not found")
+        _hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+        _hip.hipHostMalloc.restype = ctypes.c_int
+        _hip.hipHostFree.argtypes = [ctypes.c_void_p]
+        _hip.hipHostFree.restype = ctypes.c_int
+    return _hip
+
+
+HIP_HOST_MALLOC_COHERENT = 0x40000000
+
+
+class Pipeline:
+    """Buffers and streams of a chunk-pipelined transfer (device work area,
+    coherent pinned host link buffer, four streams), reusable across calls of
+    the same shape.  ``transfer(x, out)`` moves ``x`` into ``out`` through
+    the link, compressed or raw, and returns the bytes each group sent."""
+
+    def __init__(self, dtype: int, n_elems: int, codebooks, segment_elems: int, group_elems: int, depth: int,
+                 device=None, host_flags: int = HIP_HOST_MALLOC_COHERENT):
+        import torch
+        self.dtype, self.n, self.seg, self.group, self.depth = dtype, n_elems, segment_elems, group_elems, depth
+        self.cbs = np.ascontiguousarray(np.asarray(codebooks, dtype=np.uint8)).reshape(-1, 16)
+        self.work_bytes, self.link_bytes = splitzip_pipeline_sizes(dtype, n_elems, self.cbs.shape[0], segment_elems,
+                                                                   group_elems, depth)
+        self.groups = -(-n_elems // group_elems)
+        self.slot = (self.link_bytes - (-(-8 * self.groups // 256) * 256)) // depth
+        self.work = torch.empty(self.work_bytes, dtype=torch.uint8, device=device)
+        self._link = ctypes.c_void_p(0)
+        rc = _hip_runtime().hipHostMalloc(ctypes.byref(self._link), self.link_bytes, host_flags)
+        if rc != 0 or not self._link.value:
+            raise RuntimeError(f"hipHostMalloc failed ({rc})")
+        if self.work.data_ptr() % 256 or self._link.value % 256:
+            raise RuntimeError("pipeline buffers are not 256-byte aligned")
+        self.link = np.ctypeslib.as_array((ctypes.c_uint8 * self.link_bytes).from_address(self._link.value))
+        self.streams = [torch.cuda.Stream(device=device) for _ in range(4)]
+
+    def __del__(self):
+        if getattr(self, "_link", None) is not None and self._link.value:
+            _hip_runtime().hipHostFree(self._link)
+            self._link = None
+
+    def transfer(self, x, out, compress: bool = True, status=None):
+        if not x.is_contiguous() or not out.is_contiguous() or x.numel() != self.n or out.numel() != self.n:
+            raise ValueError("x and out must be contiguous with the planned element count")
+        sizes = np.zeros(self.groups, dtype=np.uint64)
+        rc = splitzip_pipeline_transfer(self.dtype, x.data_ptr(), self.n, self.cbs, self.cbs.shape[0], self.seg,
+                                        self.group, self.depth, compress, self.work.data_ptr(), self.work_bytes,
+                                        self._link.value, self.link_bytes, out.data_ptr(),
+                                        None if status is None else status.data_ptr(), sizes,
+                                        [s.cuda_stream for s in self.streams])
+        if rc != OK:
+            raise SplitZipError(rc, "splitzip_pipeline_transfer")
+        return sizes
+
+    def slot_stream(self, g: int, nbytes: int) -> np.ndarray:
+        """Bytes of group g's stream as they sit in the host link buffer
+        (valid after a transfer while g is among the last ``depth`` groups)."""
+        off = (g % self.depth) * self.slot
+        return self.link[off:off + nbytes].copy()

@@ -6,7 +6,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "splitzip.hip")
+SRCS = [os.path.join(HERE, "csrc", "splitzip.hip"), os.path.join(HERE, "csrc", "pipeline.hip")]
 LIB = os.path.join(HERE, "libsplitzip.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -24,7 +24,7 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)

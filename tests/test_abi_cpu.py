@@ -84,3 +84,30 @@ def test_product_package_does_not_import_oracle():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in text.replace("oracle`", ""), fn
+
+
+def test_pipeline_sizes_and_argument_errors():
+    # sizes: two device slots and one host slot per depth step, each slot at
+    # least the group's worst-case stream with workspace
+    G = 4 * 65536
+    d, h = sz.splitzip_pipeline_sizes(O.BF16, 10 * G + 12345, 1, 0, G, 3)
+    slot = -(-max(sz.splitzip_max_compressed_size(O.BF16, G, 1), 2 * G) // 256) * 256
+    assert d == 2 * 3 * slot and h == 3 * slot + 256  # 11 groups: 88 bytes of sizes
+    # per-layer codebooks: groups of whole segments carry several codebooks
+    seg = 2 * 65536
+    d2, _ = sz.splitzip_pipeline_sizes(O.BF16, 8 * seg, 8, seg, 2 * seg, 2)
+    assert d2 >= 4 * sz.splitzip_max_compressed_size(O.BF16, 2 * seg, 2)
+    bad = [
+        (O.BF16, 1 << 20, 1, 0, 65536, 1),        # depth 1
+        (O.BF16, 1 << 20, 1, 0, 65536, 33),       # depth > 32
+        (O.BF16, 1 << 20, 1, 0, 65536 + 8, 2),    # group not whole chunks
+        (O.BF16, 1 << 20, 1, 0, 0, 2),            # empty group
+        (7, 1 << 20, 1, 0, 65536, 2),             # dtype
+        (O.BF16, 1 << 20, 0, 0, 65536, 2),        # no codebook
+        (O.BF16, 1 << 20, 4, 3 * 65536, 2 * 65536, 2),   # group neither divides nor is divided by segment
+        (O.BF16, 1 << 20, 2, 65536, 65536, 2),    # codebooks do not cover n
+    ]
+    for args in bad:
+        with pytest.raises(sz.SplitZipError) as e:
+            sz.splitzip_pipeline_sizes(*args)
+        assert e.value.status == sz.E_INVALID, args
