@@ -131,6 +131,36 @@ int splitzip_decompress(const void* d_in, size_t in_bytes, int dtype, size_t n_e
 /* Static text for a status code. */
 const char* splitzip_status_string(int status);
 
+/* ---- On-device calibration ------------------------------------------------
+ * The pages calibrate offline, so that no histogram is built on the critical
+ * path (technical summary, "Optimizacion" and "Resultados / Calibracion";
+ * abstract).  splitzip_calibrate_device builds that histogram on the GPU, to
+ * measure what calibrating online would cost and to calibrate per tensor or
+ * per layer at run time.  The codebooks equal splitzip_calibrate's on the same
+ * samples: the 16 most frequent exponents, most frequent first, equal counts
+ * to the lower exponent, unseen exponents filling up in ascending order.
+ *
+ * splitzip_calibrate_device_work_bytes: bytes of d_work for n_codebooks
+ * segments (8 per histogram bin: 256 bins BF16, 32 E5M2), 0 for an invalid
+ * dtype or n_codebooks outside 1..65535. */
+size_t splitzip_calibrate_device_work_bytes(int dtype, uint32_t n_codebooks);
+
+/* splitzip_calibrate_device: one codebook per segment of d_samples.
+ *   d_samples       n_elems elements on the device (BF16 as uint16, E5M2 as
+ *                   uint8), 16-byte aligned.
+ *   segment_elems   elements per segment, ignored when n_codebooks == 1
+ *                   (one segment: the whole tensor); else segment k covers
+ *                   [k * segment_elems, min((k + 1) * segment_elems, n)) and
+ *                   n_codebooks * segment_elems >= n_elems.  A segment with no
+ *                   elements gets the codebook 0, 1, ..., 15.
+ *   d_codebooks_out n_codebooks x 16 bytes, device memory, written by the GPU.
+ *   d_work          work_bytes of device memory, 8-byte aligned, overwritten.
+ * Stream-ordered, three launches, no host synchronization.  Returns
+ * SPLITZIP_OK, SPLITZIP_E_INVALID, SPLITZIP_E_CAPACITY or SPLITZIP_E_HIP. */
+int splitzip_calibrate_device(int dtype, const void* d_samples, size_t n_elems, size_t segment_elems,
+                              uint32_t n_codebooks, uint8_t* d_codebooks_out, void* d_work, size_t work_bytes,
+                              hipStream_t stream);
+
 /* ---- Chunk-pipelined transfer through a host link -------------------------
  * The pages' setting is a KV cache moving from a prefill node to a decode
  * node over a 50-100 GB/s link, where the codec shrinks the transferred bytes

@@ -18,10 +18,13 @@ from ._native import (  # noqa: F401
     OK,
     Pipeline,
     SplitZipError,
+    calibrate_device,
     compress,
     decompress,
     load,
     splitzip_calibrate,
+    splitzip_calibrate_device,
+    splitzip_calibrate_device_work_bytes,
     splitzip_compress,
     splitzip_decompress,
     splitzip_max_compressed_size,

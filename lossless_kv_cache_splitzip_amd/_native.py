@@ -29,6 +29,8 @@ EXPORTS = (
     "splitzip_compress",
     "splitzip_decompress",
     "splitzip_status_string",
+    "splitzip_calibrate_device_work_bytes",
+    "splitzip_calibrate_device",
     "splitzip_pipeline_sizes",
     "splitzip_pipeline_transfer",
 )
@@ -64,6 +66,10 @@ def load():
     lib.splitzip_decompress.restype = i32
     lib.splitzip_status_string.argtypes = [i32]
     lib.splitzip_status_string.restype = ctypes.c_char_p
+    lib.splitzip_calibrate_device_work_bytes.argtypes = [i32, u32]
+    lib.splitzip_calibrate_device_work_bytes.restype = sz
+    lib.splitzip_calibrate_device.argtypes = [i32, vp, sz, sz, u32, vp, vp, sz, vp]
+    lib.splitzip_calibrate_device.restype = i32
     lib.splitzip_pipeline_sizes.argtypes = [i32, sz, u32, sz, sz, u32, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.splitzip_pipeline_sizes.restype = i32
     lib.splitzip_pipeline_transfer.argtypes = [i32, vp, sz, vp, u32, sz, sz, u32, i32, vp, sz, vp, sz, vp, vp, vp, vp]
@@ -104,6 +110,39 @@ def splitzip_decompress(d_in: int, in_bytes: int, dtype: int, n_elems: int, d_ou
                         d_status: int | None, stream: int | None) -> int:
     return int(load().splitzip_decompress(d_in or None, in_bytes, dtype, n_elems, d_out or None,
                                           d_status or None, stream or None))
+
+
+def splitzip_calibrate_device_work_bytes(dtype: int, n_codebooks: int) -> int:
+    return int(load().splitzip_calibrate_device_work_bytes(dtype, n_codebooks))
+
+
+def splitzip_calibrate_device(dtype: int, d_samples: int, n_elems: int, segment_elems: int, n_codebooks: int,
+                              d_codebooks_out: int, d_work: int, work_bytes: int, stream: int | None) -> int:
+    return int(load().splitzip_calibrate_device(dtype, d_samples or None, n_elems, segment_elems, n_codebooks,
+                                                d_codebooks_out or None, d_work or None, work_bytes,
+                                                stream or None))
+
+
+def calibrate_device(x, n_codebooks: int = 1, segment_elems: int = 0, out=None, work=None, stream=None):
+    """Codebooks of a contiguous device tensor (one per segment) computed on
+    the GPU; returns a (n_codebooks, 16) uint8 device tensor.  Nothing is
+    synchronized."""
+    import torch
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor")
+    dtype = _dtype_of(x)
+    need = splitzip_calibrate_device_work_bytes(dtype, n_codebooks)
+    if need == 0:
+        raise SplitZipError(E_INVALID, "splitzip_calibrate_device_work_bytes")
+    if out is None:
+        out = torch.empty((n_codebooks, 16), dtype=torch.uint8, device=x.device)
+    if work is None:
+        work = torch.empty(need, dtype=torch.uint8, device=x.device)
+    rc = splitzip_calibrate_device(dtype, x.data_ptr(), x.numel(), segment_elems, n_codebooks, out.data_ptr(),
+                                   work.data_ptr(), work.numel(), _stream_handle(stream))
+    if rc != OK:
+        raise SplitZipError(rc, "splitzip_calibrate_device")
+    return out
 
 
 def splitzip_pipeline_sizes(dtype: int, n_elems: int, n_codebooks: int, segment_elems: int, group_elems: int,

@@ -6,7 +6,8 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", "splitzip.hip"), os.path.join(HERE, "csrc", "pipeline.hip")]
+SRCS = [os.path.join(HERE, "csrc", "splitzip.hip"), os.path.join(HERE, "csrc", "pipeline.hip"),
+        os.path.join(HERE, "csrc", "calibrate.hip")]
 LIB = os.path.join(HERE, "libsplitzip.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -111,3 +111,25 @@ def test_pipeline_sizes_and_argument_errors():
         with pytest.raises(sz.SplitZipError) as e:
             sz.splitzip_pipeline_sizes(*args)
         assert e.value.status == sz.E_INVALID, args
+
+
+def test_calibrate_device_work_bytes_and_argument_errors():
+    assert sz.splitzip_calibrate_device_work_bytes(O.BF16, 1) == 256 * 8
+    assert sz.splitzip_calibrate_device_work_bytes(O.E5M2, 80) == 80 * 32 * 8
+    assert sz.splitzip_calibrate_device_work_bytes(O.BF16, 0) == 0
+    assert sz.splitzip_calibrate_device_work_bytes(9, 1) == 0
+    # rejected on the host before any GPU work: fake (never dereferenced)
+    # 16-aligned addresses
+    p, w = 1 << 20, 1 << 21
+    cases = [
+        ((O.BF16, 0, 100, 0, 1, p, w, 4096, None), sz.E_INVALID),       # null samples
+        ((O.BF16, p + 2, 100, 0, 1, p, w, 4096, None), sz.E_INVALID),   # misaligned samples
+        ((O.BF16, p, 100, 0, 1, 0, w, 4096, None), sz.E_INVALID),       # null output
+        ((O.BF16, p, 100, 0, 1, p, 0, 4096, None), sz.E_INVALID),       # null work
+        ((O.BF16, p, 100, 0, 1, p, w, 100, None), sz.E_CAPACITY),       # work too small
+        ((O.BF16, p, 100, 10, 4, p, w, 1 << 16, None), sz.E_INVALID),   # segments do not cover n
+        ((O.BF16, p, 100, 0, 4, p, w, 1 << 16, None), sz.E_INVALID),    # K > 1 needs a segment length
+        ((7, p, 100, 0, 1, p, w, 4096, None), sz.E_INVALID),            # dtype
+    ]
+    for args, want in cases:
+        assert sz.splitzip_calibrate_device(*args) == want, args
