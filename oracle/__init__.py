@@ -81,6 +81,14 @@ def _bind(lib):
     lib.szo_count_escapes.restype = u64
     lib.szo_sections.argtypes = [i32, u64, u32, vp]
     lib.szo_sections.restype = i32
+    lib.szo_variant_stream_size.argtypes = [i32, u64, u32, u64]
+    lib.szo_variant_stream_size.restype = u64
+    lib.szo_variant_max_size.argtypes = [i32, u64, u32]
+    lib.szo_variant_max_size.restype = u64
+    lib.szo_variant_compress.argtypes = [i32, vp, u64, vp, u32, u64, vp, u64, ctypes.POINTER(u64)]
+    lib.szo_variant_compress.restype = i32
+    lib.szo_variant_decompress.argtypes = [i32, vp, u64, u64, vp]
+    lib.szo_variant_decompress.restype = i32
     return lib
 
 
@@ -181,3 +189,44 @@ def count_escapes(dtype: int, x, codebooks, segment_elems: int = 0) -> int:
     a = _as_elems(x, dtype)
     cbs = _as_codebooks(codebooks)
     return int(_load().szo_count_escapes(dtype, _ptr(a), a.size, _ptr(cbs), cbs.shape[0], segment_elems))
+
+
+# ---- ablation variants (BF16): 1 = top-15 + sentinel, 2 = top-8 (3-bit codes)
+SENTINEL = 1
+TOP8 = 2
+
+
+def variant_stream_size(variant: int, n: int, K: int, E: int) -> int:
+    return int(_load().szo_variant_stream_size(variant, n, K, E))
+
+
+def variant_max_size(variant: int, n: int, K: int) -> int:
+    return int(_load().szo_variant_max_size(variant, n, K))
+
+
+def variant_compress(variant: int, x, codebooks, segment_elems: int = 0) -> np.ndarray:
+    a = _as_elems(x, BF16)
+    cbs = _as_codebooks(codebooks)
+    K = cbs.shape[0]
+    cap = max(variant_max_size(variant, a.size, max(K, 1)), 1)
+    out = np.zeros(cap, dtype=np.uint8)
+    nbytes = ctypes.c_uint64(0)
+    rc = _load().szo_variant_compress(variant, _ptr(a), a.size, _ptr(cbs) if cbs.size else None, K, segment_elems,
+                                      _ptr(out), cap, ctypes.byref(nbytes))
+    if rc != OK:
+        raise ValueError(f"szo_variant_compress failed: {rc}")
+    return out[:nbytes.value].copy()
+
+
+def variant_decompress_rc(variant: int, stream, n: int):
+    s = np.ascontiguousarray(np.asarray(stream, dtype=np.uint8))
+    out = np.zeros(max(n, 1), dtype=np.uint16)
+    rc = int(_load().szo_variant_decompress(variant, _ptr(s), s.size, n, _ptr(out)))
+    return rc, (out[:n] if rc == OK else None)
+
+
+def variant_decompress(variant: int, stream, n: int) -> np.ndarray:
+    rc, y = variant_decompress_rc(variant, stream, n)
+    if rc != OK:
+        raise ValueError(f"szo_variant_decompress failed: {rc}")
+    return y

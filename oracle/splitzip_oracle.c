@@ -451,3 +451,210 @@ uint64_t szo_count_escapes(int dtype, const void *in, uint64_t n, const uint8_t 
   }
   return E;
 }
+
+/* ---- Ablation variants (BF16), the two designs the pages compare against
+ * the top-16 codec ([TS] Metodologia / Decision de Diseno and Resultados):
+ *
+ *   variant 1, top-15 + sentinel: codes 0..14 are the 15 most frequent
+ *     exponents (codebook entries 0..14) and code 15 marks an escape.  The
+ *     escape stream holds only the raw exponents, in element order; an
+ *     escape's position is where its sentinel sits.  The pages say this
+ *     saves metadata but makes decoding irregular (3.5x slower).
+ *   variant 2, top-8: 3-bit codes for the 8 most frequent exponents
+ *     (entries 0..7); the pages report 92% coverage instead of 99.8% and a
+ *     3x slower decode.
+ *
+ * What the pages leave open, and the reading taken here:
+ *   V1 layout: the main layout with the variant id in header byte 48; the
+ *      per-chunk escape offsets are kept in both (a chunk-parallel decoder
+ *      needs them; 8 bytes per 65536 elements).
+ *   V2 top-15: an escaped element's nibble is 15; the escape section is E
+ *      bytes of raw exponents (no positions).
+ *   V3 top-8: codes are packed 8 per 3 little-endian bytes, element j of a
+ *      group at bits 3j (as the E5M2 triples, R7); an escaped element's code
+ *      is 0 and its escape is a 3-byte record as in R6.
+ *   V4 codebooks: 16 distinct entries are stored per segment as in the main
+ *      format; the variant uses the first 15 or 8.
+ *   Sections (A = round up to 256): N0 = A(64 + 16K + 8(C+1)); codes;
+ *   N1 = N0 + A(code bytes); sign|mantissa n bytes; P = N1 + A(n);
+ *   S = P + E (top-15) or P + 3E (top-8). */
+#define SZO_V_SENTINEL 1
+#define SZO_V_TOP8 2
+
+static int variant_ok(int v) { return v == SZO_V_SENTINEL || v == SZO_V_TOP8; }
+static uint64_t variant_code_bytes(int v, uint64_t n) { return v == SZO_V_TOP8 ? 3ull * ceil_div(n, 8) : ceil_div(n, 2); }
+static uint64_t variant_record_bytes(int v) { return v == SZO_V_SENTINEL ? 1ull : 3ull; }
+static unsigned variant_codes(int v) { return v == SZO_V_SENTINEL ? 15u : 8u; }
+
+static szo_layout variant_layout(int v, uint64_t n, uint64_t K) {
+  szo_layout L;
+  L.C = ceil_div(n, SZO_CHUNK);
+  L.N0 = align256(64 + 16 * K + 8 * (L.C + 1));
+  L.N1 = L.N0 + align256(variant_code_bytes(v, n));
+  L.P = L.N1 + align256(n);
+  return L;
+}
+
+uint64_t szo_variant_stream_size(int v, uint64_t n, uint32_t K, uint64_t E) {
+  if (!variant_ok(v)) return 0;
+  return variant_layout(v, n, K).P + variant_record_bytes(v) * E;
+}
+
+uint64_t szo_variant_max_size(int v, uint64_t n, uint32_t K) { return szo_variant_stream_size(v, n, K, n); }
+
+/* Code of exponent e among the variant's first entries, or -1. */
+static int variant_code_of(int v, const uint8_t *cb, unsigned e) {
+  for (unsigned k = 0; k < variant_codes(v); ++k)
+    if (cb[k] == e) return (int)k;
+  return -1;
+}
+
+/* Code of element i in the code section. */
+static unsigned variant_get_code(int v, const uint8_t *codes, uint64_t i) {
+  if (v == SZO_V_SENTINEL) return (i % 2 == 0) ? (codes[i / 2] & 0xFu) : (codes[i / 2] >> 4);
+  uint64_t q = i / 8, j = i % 8;
+  uint64_t g = codes[3 * q] | ((uint64_t)codes[3 * q + 1] << 8) | ((uint64_t)codes[3 * q + 2] << 16);
+  return (unsigned)((g >> (3 * j)) & 0x7u);
+}
+
+static void variant_put_code(int v, uint8_t *codes, uint64_t i, unsigned code) {
+  if (v == SZO_V_SENTINEL) {
+    if (i % 2 == 0)
+      codes[i / 2] = (uint8_t)(codes[i / 2] | code);
+    else
+      codes[i / 2] = (uint8_t)(codes[i / 2] | (code << 4));
+    return;
+  }
+  uint64_t q = i / 8, j = i % 8;
+  uint64_t g = codes[3 * q] | ((uint64_t)codes[3 * q + 1] << 8) | ((uint64_t)codes[3 * q + 2] << 16);
+  g |= (uint64_t)code << (3 * j);
+  codes[3 * q] = (uint8_t)g;
+  codes[3 * q + 1] = (uint8_t)(g >> 8);
+  codes[3 * q + 2] = (uint8_t)(g >> 16);
+}
+
+int szo_variant_compress(int v, const void *in, uint64_t n, const uint8_t *cbs, uint32_t K, uint64_t seg,
+                         uint8_t *out, uint64_t capacity, uint64_t *out_bytes) {
+  if (!variant_ok(v)) return SZO_E_INVALID;
+  int rc = compress_args_ok(SZO_BF16, in, n, cbs, K, seg);
+  if (rc != SZO_OK) return rc;
+  if (out == NULL) return SZO_E_INVALID;
+  if (capacity < szo_variant_max_size(v, n, K)) return SZO_E_CAPACITY;
+  szo_layout L = variant_layout(v, n, K);
+  memset(out, 0, L.P);
+  uint8_t *codes = out + L.N0;
+  uint8_t *sm = out + L.N1;
+  uint8_t *esc = out + L.P;
+  uint8_t *off = out + 64 + 16ull * K;
+  uint64_t E = 0;
+  for (uint64_t c = 0; c < L.C; ++c) {
+    const uint8_t *cb = cbs + 16ull * chunk_codebook(c, K, seg);
+    uint64_t first = c * SZO_CHUNK;
+    uint64_t last = first + SZO_CHUNK < n ? first + SZO_CHUNK : n;
+    put_u64(off + 8 * c, E);
+    for (uint64_t i = first; i < last; ++i) {
+      unsigned e = get_exponent(SZO_BF16, in, i);
+      int code = variant_code_of(v, cb, e);
+      unsigned written;
+      if (code >= 0) {
+        written = (unsigned)code;
+      } else if (v == SZO_V_SENTINEL) {
+        written = 15; /* V2 */
+        esc[E] = (uint8_t)e;
+        E += 1;
+      } else {
+        written = 0; /* V3 */
+        put_u16(esc + 3 * E, i - first);
+        esc[3 * E + 2] = (uint8_t)e;
+        E += 1;
+      }
+      variant_put_code(v, codes, i, written);
+      sm[i] = (uint8_t)get_signmant(SZO_BF16, in, i);
+    }
+  }
+  put_u64(off + 8 * L.C, E);
+  uint64_t S = L.P + variant_record_bytes(v) * E;
+  put_u32(out + 0, 0x00315A53u);
+  put_u16(out + 4, 1);
+  out[6] = (uint8_t)SZO_BF16;
+  out[7] = 16;
+  put_u64(out + 8, n);
+  put_u64(out + 16, E);
+  put_u64(out + 24, S);
+  put_u32(out + 32, L.C);
+  put_u32(out + 36, K);
+  put_u64(out + 40, K == 1 ? n : seg);
+  out[48] = (uint8_t)v; /* V1 */
+  memcpy(out + 64, cbs, 16ull * K);
+  if (out_bytes) *out_bytes = S;
+  return SZO_OK;
+}
+
+int szo_variant_decompress(int v, const uint8_t *in, uint64_t in_bytes, uint64_t n, void *out) {
+  if (!variant_ok(v) || in == NULL || (out == NULL && n > 0)) return SZO_E_INVALID;
+  /* header */
+  if (in_bytes < 64 || get_u32(in) != 0x00315A53u || get_u16(in + 4) != 1 || in[6] != SZO_BF16 || in[7] != 16 ||
+      get_u64(in + 8) != n || in[48] != v)
+    return SZO_E_CORRUPT;
+  for (int k = 49; k < 64; ++k)
+    if (in[k] != 0) return SZO_E_CORRUPT;
+  uint64_t E = get_u64(in + 16), S = get_u64(in + 24), C = get_u32(in + 32), K = get_u32(in + 36);
+  uint64_t seg = get_u64(in + 40);
+  if (C != ceil_div(n, SZO_CHUNK) || K == 0 || K > SZO_MAX_K) return SZO_E_CORRUPT;
+  if (K == 1 ? seg != n : (seg == 0 || seg % SZO_CHUNK != 0 || seg < ceil_div(n, K))) return SZO_E_CORRUPT;
+  if (E > n) return SZO_E_CORRUPT;
+  szo_layout L = variant_layout(v, n, K);
+  if (S != L.P + variant_record_bytes(v) * E || S > in_bytes) return SZO_E_CORRUPT;
+  for (uint64_t k = 0; k < K; ++k)
+    if (!codebook_valid(SZO_BF16, in + 64 + 16 * k)) return SZO_E_CORRUPT;
+  const uint8_t *off = in + 64 + 16 * K;
+  const uint8_t *codes = in + L.N0;
+  const uint8_t *sm = in + L.N1;
+  const uint8_t *esc = in + L.P;
+  if (get_u64(off) != 0 || get_u64(off + 8 * C) != E) return SZO_E_CORRUPT;
+  for (uint64_t c = 0; c < C; ++c) {
+    uint64_t lo = get_u64(off + 8 * c), hi = get_u64(off + 8 * (c + 1));
+    if (lo > hi || hi > E) return SZO_E_CORRUPT;
+    uint64_t first = c * SZO_CHUNK;
+    uint64_t last = first + SZO_CHUNK < n ? first + SZO_CHUNK : n;
+    if (v == SZO_V_SENTINEL) {
+      uint64_t sentinels = 0;
+      for (uint64_t i = first; i < last; ++i) sentinels += variant_get_code(v, codes, i) == 15;
+      if (sentinels != hi - lo) return SZO_E_CORRUPT;
+    } else {
+      for (uint64_t r = lo; r < hi; ++r) {
+        uint64_t pos = get_u16(esc + 3 * r);
+        if (pos >= last - first) return SZO_E_CORRUPT;
+        if (r > lo && pos <= get_u16(esc + 3 * (r - 1))) return SZO_E_CORRUPT;
+      }
+    }
+  }
+  /* dense pass, then (top-8) the escape overwrite */
+  for (uint64_t c = 0; c < C; ++c) {
+    const uint8_t *cb = in + 64 + 16 * chunk_codebook(c, K, seg);
+    uint64_t first = c * SZO_CHUNK;
+    uint64_t last = first + SZO_CHUNK < n ? first + SZO_CHUNK : n;
+    uint64_t r = get_u64(off + 8 * c);
+    for (uint64_t i = first; i < last; ++i) {
+      unsigned code = variant_get_code(v, codes, i);
+      unsigned e;
+      if (v == SZO_V_SENTINEL && code == 15) {
+        e = esc[r]; /* the r-th escape of the stream belongs to the r-th sentinel */
+        r += 1;
+      } else {
+        e = cb[code];
+      }
+      put_element(SZO_BF16, out, i, e, sm[i]);
+    }
+  }
+  if (v == SZO_V_TOP8) {
+    for (uint64_t c = 0; c < C; ++c) {
+      uint64_t lo = get_u64(off + 8 * c), hi = get_u64(off + 8 * (c + 1));
+      for (uint64_t r = lo; r < hi; ++r) {
+        uint64_t i = c * SZO_CHUNK + get_u16(esc + 3 * r);
+        put_element(SZO_BF16, out, i, esc[3 * r + 2], get_signmant(SZO_BF16, out, i));
+      }
+    }
+  }
+  return SZO_OK;
+}

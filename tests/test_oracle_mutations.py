@@ -12,6 +12,7 @@ import pytest
 
 import oracle as O
 import test_oracle_pins as P
+import test_oracle_variants as PV
 
 SRC = os.path.join(os.path.dirname(O.__file__), "splitzip_oracle.c")
 
@@ -34,9 +35,17 @@ MUTATIONS = {
     "calibrate_skips_last_value": ("for (unsigned v = 0; v < V; ++v) {\n      if (chosen[v]) continue;",
                                    "for (unsigned v = 0; v + 1 < V; ++v) {\n      if (chosen[v]) continue;"),
     "chunk_codebook_index": ("return (c * SZO_CHUNK) / seg;", "return c / seg;"),
-    "offsets_inclusive": ("    put_u64(off + 8 * c, E);\n    for", "    for"),
+    "offsets_inclusive": ("    put_u64(off + 8 * c, E);\n    for (uint64_t i = first; i < last; ++i) {\n      unsigned e = get_exponent(dtype, in, i);",
+                          "    for (uint64_t i = first; i < last; ++i) {\n      unsigned e = get_exponent(dtype, in, i);"),
     "no_section_alignment": ("return (x + 255ull) / 256ull * 256ull;", "return x;"),
     "total_bytes_field": ("put_u64(out + 24, L.P + 3 * E);", "put_u64(out + 24, L.P + 2 * E);"),
+    # ablation variants
+    "sentinel_code_14": ("written = 15; /* V2 */", "written = 14; /* V2 */"),
+    "top8_uses_seven_codes": ("return v == SZO_V_SENTINEL ? 15u : 8u;", "return v == SZO_V_SENTINEL ? 15u : 7u;"),
+    "top8_code_order_reversed": ("g |= (uint64_t)code << (3 * j);", "g |= (uint64_t)code << (3 * (7 - j));"),
+    "sentinel_values_from_stream_start": ("    uint64_t r = get_u64(off + 8 * c);\n    for (uint64_t i = first; i < last; ++i) {\n      unsigned code",
+                                          "    uint64_t r = 0;\n    for (uint64_t i = first; i < last; ++i) {\n      unsigned code"),
+    "variant_byte_missing": ("out[48] = (uint8_t)v; /* V1 */", "(void)v; /* V1 */"),
 }
 
 PINS = [
@@ -52,6 +61,12 @@ PINS = [
     P.test_bf16_split_matches_float_semantics,
     P.test_explainer_position50_golden,
     P.test_error_paths,
+    lambda: PV.test_exhaustive_round_trip(O.SENTINEL),
+    lambda: PV.test_exhaustive_round_trip(O.TOP8),
+    lambda: PV.test_escape_sets_and_order_against_numpy(O.SENTINEL),
+    lambda: PV.test_escape_sets_and_order_against_numpy(O.TOP8),
+    PV.test_hand_worked_sentinel_stream,
+    PV.test_hand_worked_top8_stream,
 ]
 
 
