@@ -218,6 +218,46 @@ def calibrate_leg(wl, seg, cbs, stream, reps: int = 10):
                          "unit": "GB/s", "frac": wl.raw_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS}}
 
 
+def ablation_leg(wl, cbs, seg, stream, main_enc_ms, main_dec_ms, reps: int = 10):
+    """The pages' two rejected designs on the same workload (BF16 only):
+    top-15 + sentinel and top-8 3-bit codes.  Event-timed mean of `reps`
+    compress and decompress calls after a checked warm-up round trip."""
+    import numpy as np
+    import torch
+
+    import lossless_kv_cache_splitzip_amd as sz
+
+    res = {}
+    for name, v in (("top15_sentinel", sz.VARIANT_TOP15_SENTINEL), ("top8", sz.VARIANT_TOP8)):
+        out, nb = sz.variant_compress(v, wl.data, cbs, seg, stream=stream)
+        dec = torch.empty_like(wl.data)
+        status = torch.zeros(1, dtype=torch.int32, device=wl.data.device)
+        sz.variant_decompress(v, out, wl.n, out=dec, status=status, stream=stream)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0 and torch.equal(dec.view(torch.uint8), wl.data.view(torch.uint8))
+        n_bytes = int(nb.item())
+        n_esc = int(np.frombuffer(out[16:24].cpu().numpy().tobytes(), "<u8")[0])
+        times = {}
+        for what in ("enc", "dec"):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                if what == "enc":
+                    sz.variant_compress(v, wl.data, cbs, seg, out=out, out_bytes=nb, stream=stream)
+                else:
+                    sz.variant_decompress(v, out, wl.n, out=dec, status=status, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[what] = e0.elapsed_time(e1) / reps
+        res[name] = {"compression_ratio": wl.raw_bytes / n_bytes, "escape_rate": n_esc / wl.n,
+                     "encode_ms": times["enc"], "decode_ms": times["dec"],
+                     "decode_GBps": wl.raw_bytes / (times["dec"] / 1e3) / 1e9,
+                     "decode_slowdown_vs_top16": times["dec"] / main_dec_ms,
+                     "encode_slowdown_vs_top16": times["enc"] / main_enc_ms}
+        del out, dec
+    return res
+
+
 def kvsynth_bits(t):
     import kvsynth
     return kvsynth.to_numpy_bits(t)
@@ -320,6 +360,11 @@ def main():
     sfx = "bf16" if dtype == kvsynth.BF16 else "e5m2"
     enc_kernels = ["prep_kernel", f"encode_dense_{sfx}_kernel", "encode_sums_kernel", f"encode_place_{sfx}_kernel"]
     dname = f"decode_{sfx}_kernel"
+    abl = ablation_leg(wl, cbs, seg, stream, enc_ms, dec_ms) if dtype == kvsynth.BF16 else None
+    if abl:
+        for k, r in abl.items():
+            log(f"[bench] {k}: ratio {r['compression_ratio']:.4f}, escapes {100 * r['escape_rate']:.2f}%, "
+                f"decode {r['decode_ms']:.3f} ms ({r['decode_slowdown_vs_top16']:.2f}x top-16)")
     calib = calibrate_leg(wl, seg, cbs, stream)
     log(f"[bench] device calibration of {calib['codebooks']} codebooks: {calib['ms']:.3f} ms "
         f"({calib['GBps']:.0f} GB/s)")
@@ -366,6 +411,7 @@ def main():
         "cpu_baseline": cpu,
         "link_transfer": link,
         "calibrate_device": calib,
+        "ablations": abl,
         "cpu_baseline_parallel": cpu_par,
         "pages_context": {"encode_GBps": 613.3, "decode_GBps": 2181.8, "hardware": "not stated in the pages"},
         "kernel_source_sha256_16": source_digest(),

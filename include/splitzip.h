@@ -131,6 +131,38 @@ int splitzip_decompress(const void* d_in, size_t in_bytes, int dtype, size_t n_e
 /* Static text for a status code. */
 const char* splitzip_status_string(int status);
 
+/* ---- Ablation variants (BF16) ---------------------------------------------
+ * The two designs the pages measure against the top-16 codec (technical
+ * summary, "Metodologia / Decision de Diseno" and "Resultados"), as streams
+ * of their own, to compare decode speed and size on this GPU:
+ *   SPLITZIP_VARIANT_TOP15_SENTINEL  codebook entries 0..14 get codes 0..14;
+ *     code 15 marks an escape, whose raw exponent is the next byte of the
+ *     escape section (no positions: the pages' "saves metadata" design).
+ *   SPLITZIP_VARIANT_TOP8            codebook entries 0..7 get 3-bit codes,
+ *     8 codes per 3 little-endian bytes (element j at bit 3j); escapes are the
+ *     codec's 3-byte position records.
+ * Layout: the SZ1 layout with header byte 48 = the variant, the code section
+ * of ceil(n/2) (top-15) or 3 ceil(n/8) (top-8) bytes, and E escape bytes
+ * (top-15) or 3E (top-8) at the end.  Codebooks are 16 distinct entries per
+ * segment as for splitzip_compress; the variant uses the first 15 or 8.
+ * The arguments, alignment, workspace and status conventions are those of
+ * splitzip_max_compressed_size, splitzip_compress and splitzip_decompress;
+ * dtype is BF16.  An invalid variant returns 0 / SPLITZIP_E_INVALID. */
+typedef enum { SPLITZIP_VARIANT_TOP15_SENTINEL = 1, SPLITZIP_VARIANT_TOP8 = 2 } splitzip_variant;
+
+size_t splitzip_variant_max_compressed_size(int variant, size_t n_elems, uint32_t n_codebooks);
+
+int splitzip_variant_compress(int variant, const void* d_in, size_t n_elems, const uint8_t* h_codebooks,
+                              uint32_t n_codebooks, size_t segment_elems, void* d_out, size_t out_capacity,
+                              uint64_t* d_out_bytes, hipStream_t stream);
+
+/* Top-8: one workgroup per 8192-element tile, as splitzip_decompress.
+ * Top-15 + sentinel: one workgroup per chunk, which counts the sentinels
+ * before every element to find its value (the irregular step the pages
+ * attribute the design's slower decode to). */
+int splitzip_variant_decompress(int variant, const void* d_in, size_t in_bytes, size_t n_elems, void* d_out,
+                                int32_t* d_status, hipStream_t stream);
+
 /* ---- On-device calibration ------------------------------------------------
  * The pages calibrate offline, so that no histogram is built on the critical
  * path (technical summary, "Optimizacion" and "Resultados / Calibracion";

@@ -16,6 +16,8 @@ from ._native import (  # noqa: F401
     FP8_E5M2,
     LIB_PATH,
     OK,
+    VARIANT_TOP15_SENTINEL,
+    VARIANT_TOP8,
     Pipeline,
     SplitZipError,
     calibrate_device,
@@ -31,4 +33,7 @@ from ._native import (  # noqa: F401
     splitzip_pipeline_sizes,
     splitzip_pipeline_transfer,
     status_string,
+    splitzip_variant_max_compressed_size,
+    variant_compress,
+    variant_decompress,
 )

@@ -22,6 +22,8 @@ E_CAPACITY = -2
 E_CODEBOOK = -3
 E_CORRUPT = -4
 E_HIP = -5
+VARIANT_TOP15_SENTINEL = 1
+VARIANT_TOP8 = 2
 
 EXPORTS = (
     "splitzip_calibrate",
@@ -29,6 +31,9 @@ EXPORTS = (
     "splitzip_compress",
     "splitzip_decompress",
     "splitzip_status_string",
+    "splitzip_variant_max_compressed_size",
+    "splitzip_variant_compress",
+    "splitzip_variant_decompress",
     "splitzip_calibrate_device_work_bytes",
     "splitzip_calibrate_device",
     "splitzip_pipeline_sizes",
@@ -66,6 +71,12 @@ def load():
     lib.splitzip_decompress.restype = i32
     lib.splitzip_status_string.argtypes = [i32]
     lib.splitzip_status_string.restype = ctypes.c_char_p
+    lib.splitzip_variant_max_compressed_size.argtypes = [i32, sz, u32]
+    lib.splitzip_variant_max_compressed_size.restype = sz
+    lib.splitzip_variant_compress.argtypes = [i32, vp, sz, vp, u32, sz, vp, sz, vp, vp]
+    lib.splitzip_variant_compress.restype = i32
+    lib.splitzip_variant_decompress.argtypes = [i32, vp, sz, sz, vp, vp, vp]
+    lib.splitzip_variant_decompress.restype = i32
     lib.splitzip_calibrate_device_work_bytes.argtypes = [i32, u32]
     lib.splitzip_calibrate_device_work_bytes.restype = sz
     lib.splitzip_calibrate_device.argtypes = [i32, vp, sz, sz, u32, vp, vp, sz, vp]
@@ -110,6 +121,51 @@ def splitzip_decompress(d_in: int, in_bytes: int, dtype: int, n_elems: int, d_ou
                         d_status: int | None, stream: int | None) -> int:
     return int(load().splitzip_decompress(d_in or None, in_bytes, dtype, n_elems, d_out or None,
                                           d_status or None, stream or None))
+
+
+def splitzip_variant_max_compressed_size(variant: int, n_elems: int, n_codebooks: int) -> int:
+    return int(load().splitzip_variant_max_compressed_size(variant, n_elems, n_codebooks))
+
+
+def variant_compress(variant: int, x, codebooks, segment_elems: int = 0, out=None, out_bytes=None, stream=None):
+    """Compress a contiguous BF16 device tensor into an ablation-variant
+    stream; returns (out, out_bytes) as ``compress``."""
+    import torch
+    if not x.is_cuda or not x.is_contiguous() or _dtype_of(x) != BF16:
+        raise ValueError("x must be a contiguous BF16 device tensor")
+    cbs = np.ascontiguousarray(np.asarray(codebooks, dtype=np.uint8)).reshape(-1, 16)
+    k = cbs.shape[0]
+    cap = splitzip_variant_max_compressed_size(variant, x.numel(), k)
+    if cap == 0:
+        raise SplitZipError(E_INVALID, "splitzip_variant_max_compressed_size")
+    if out is None:
+        out = torch.empty(cap, dtype=torch.uint8, device=x.device)
+    if out_bytes is None:
+        out_bytes = torch.zeros(1, dtype=torch.int64, device=x.device)
+    rc = load().splitzip_variant_compress(variant, x.data_ptr(), x.numel(), cbs.ctypes.data, k, segment_elems,
+                                          out.data_ptr(), out.numel(), out_bytes.data_ptr(), _stream_handle(stream))
+    if rc != OK:
+        raise SplitZipError(rc, "splitzip_variant_compress")
+    return out, out_bytes
+
+
+def variant_decompress(variant: int, stream_buf, n_elems: int, out=None, status=None, in_bytes: int | None = None,
+                       stream=None):
+    """Decode an ablation-variant stream held in a uint8 device tensor;
+    returns (out, status) as ``decompress``."""
+    import torch
+    if not stream_buf.is_cuda or not stream_buf.is_contiguous():
+        raise ValueError("stream must be a contiguous device tensor")
+    if out is None:
+        out = torch.empty(n_elems, dtype=torch.int16, device=stream_buf.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=stream_buf.device)
+    nbytes = stream_buf.numel() if in_bytes is None else in_bytes
+    rc = load().splitzip_variant_decompress(variant, stream_buf.data_ptr(), nbytes, n_elems, out.data_ptr(),
+                                            status.data_ptr(), _stream_handle(stream))
+    if rc != OK:
+        raise SplitZipError(rc, "splitzip_variant_decompress")
+    return out, status
 
 
 def splitzip_calibrate_device_work_bytes(dtype: int, n_codebooks: int) -> int:

@@ -52,6 +52,12 @@ constexpr uint64_t kMaxN = 1ull << 40;
 constexpr int kCbPerPrep = 128;
 constexpr uint8_t kEsc = 0x10;  // table entry of an exponent outside the codebook
 
+// Stream variants: the codec, and the two designs the pages compare it with
+// (BF16 only): top-15 codes with code 15 as an escape sentinel and escapes
+// stored as raw exponents only, and top-8 3-bit codes with the codec's
+// position records.  Header byte 48 holds the variant (0 in the codec).
+constexpr int kMain = 0, kSentinel = 1, kTop8 = 2;
+
 __host__ __device__ inline uint64_t round256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 __host__ __device__ inline uint64_t divup(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
@@ -63,25 +69,27 @@ __device__ inline uint32_t codebook_of_chunk(uint64_t c, uint64_t seg_chunks) {
 }
 
 struct Sections {
-  uint64_t chunks, offsets, nib, sm, esc, sm_bytes;
+  uint64_t chunks, offsets, nib, sm, esc, sm_bytes, rec;  // nib: the code section; rec: bytes per escape
 };
 
-__host__ __device__ inline Sections sections_of(int dtype, uint64_t n, uint64_t k) {
+__host__ __device__ inline Sections sections_of(int dtype, uint64_t n, uint64_t k, int variant = kMain) {
   Sections s;
   s.chunks = divup(n, kChunk);
   s.offsets = 64 + 16 * k;
   s.nib = round256(s.offsets + 8 * (s.chunks + 1));
   s.sm_bytes = dtype == SPLITZIP_BF16 ? n : 3 * divup(n, 8);
-  s.sm = s.nib + round256(divup(n, 2));
+  s.sm = s.nib + round256(variant == kTop8 ? 3 * divup(n, 8) : divup(n, 2));
   s.esc = s.sm + round256(s.sm_bytes);
+  s.rec = variant == kSentinel ? 1 : 3;
   return s;
 }
 
 // Encoder workspace, after the largest possible stream: u64 escapes per
 // block of 64 tiles, u32 escapes per tile, then per tile a staging slot of
 // 512 u32 records.
-__host__ __device__ inline uint64_t workspace_offset(int dtype, uint64_t n, uint64_t k) {
-  return round256(sections_of(dtype, n, k).esc + 3 * n);
+__host__ __device__ inline uint64_t workspace_offset(int dtype, uint64_t n, uint64_t k, int variant) {
+  const Sections s = sections_of(dtype, n, k, variant);
+  return round256(s.esc + s.rec * n);
 }
 
 struct Workspace {
@@ -92,10 +100,10 @@ struct Workspace {
   uint64_t end;  // bytes from the stream start
 };
 
-__host__ inline Workspace workspace_of(uint8_t* out, int dtype, uint64_t n, uint64_t k) {
+__host__ inline Workspace workspace_of(uint8_t* out, int dtype, uint64_t n, uint64_t k, int variant = kMain) {
   const uint64_t tiles = divup(n, 8192), blocks = divup(tiles, 64);
   Workspace w;
-  uint64_t at = workspace_offset(dtype, n, k);
+  uint64_t at = workspace_offset(dtype, n, k, variant);
   w.block_sum = reinterpret_cast<uint64_t*>(out + at);
   w.super_sum = w.block_sum + blocks;
   at = round256(at + 8 * (blocks + divup(blocks, 64)));
@@ -188,9 +196,9 @@ __device__ inline uint32_t lut4(uint32_t s, uint32_t l0, uint32_t l1, uint32_t l
 // ------------------------------------------------------------- prep kernel
 struct PrepArgs {
   uint8_t* out;
-  uint64_t n, seg_stored, nib, sm, esc, sm_bytes, offsets, chunks;
+  uint64_t n, seg_stored, nib, sm, esc, sm_bytes, offsets, chunks, code_bytes;
   uint64_t* out_bytes;
-  uint32_t k, dtype, cb_first, cb_count, main;
+  uint32_t k, dtype, cb_first, cb_count, main, variant;
   uint8_t cbs[kCbPerPrep * 16];
 };
 
@@ -207,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   if (!a.main || blockIdx.x != 0) return;
   const uint32_t t = threadIdx.x;
   // zero padding after the offsets, the nibbles and the sign|mantissa bytes
-  const uint64_t ends[3] = {a.offsets + 8 * (a.chunks + 1), a.nib + divup(a.n, 2), a.sm + a.sm_bytes};
+  const uint64_t ends[3] = {a.offsets + 8 * (a.chunks + 1), a.nib + a.code_bytes, a.sm + a.sm_bytes};
   const uint64_t stops[3] = {a.nib, a.sm, a.esc};
   for (int r = 0; r < 3; ++r)
     if (ends[r] + t < stops[r]) a.out[ends[r] + t] = 0;
@@ -224,6 +232,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     else if (t < 36) { v = a.chunks; off = t - 32; }
     else if (t < 40) { v = a.k; off = t - 36; }
     else if (t < 48) { v = a.seg_stored; off = t - 40; }
+    else if (t == 48) { v = a.variant; }
     a.out[t] = (uint8_t)(v >> (8 * off));
   }
   if (a.n == 0 && t == 0) {
@@ -303,11 +312,17 @@ __device__ inline uint32_t block_exclusive_sum(uint64_t* red, uint32_t v, uint32
   return pre + inc - v;
 }
 
+// Exponent -> code table of codebook cbi: the first `codes` entries get their
+// code, every other exponent the escape entry (kEsc; with the sentinel
+// variant kEsc | 15, so an escape's nibble is the sentinel).
+template <int kVariant = kMain>
 __device__ inline void build_table(const EncArgs& a, EncShared& sh, uint64_t cbi, uint32_t entries) {
+  constexpr uint32_t kCodes = kVariant == kSentinel ? 15 : kVariant == kTop8 ? 8 : 16;
+  constexpr uint8_t kEscEntry = kVariant == kSentinel ? (kEsc | 15) : kEsc;
   const uint32_t tid = threadIdx.x;
-  if (tid < entries) sh.table[tid] = kEsc;
+  if (tid < entries) sh.table[tid] = kEscEntry;
   __syncthreads();
-  if (tid < 16) sh.table[a.out[64 + 16 * cbi + tid]] = (uint8_t)tid;
+  if (tid < kCodes) sh.table[a.out[64 + 16 * cbi + tid]] = (uint8_t)tid;
   __syncthreads();
   if (entries == 32) {  // E5M2 per-position words, from the exponent table
     const uint32_t b = tid & 0xFFu;
@@ -411,8 +426,16 @@ __device__ inline uint32_t pack_codes8(uint32_t c_lo, uint32_t c_hi) {
   return perm(v, u, 0x06040200u);
 }
 
+// Four table bytes (code in bits 0..2 of each) -> 12 bits, code k at bit 3k.
+__device__ inline uint32_t codes12(uint32_t w) {
+  const uint32_t t = w & 0x07070707u;
+  const uint32_t v = t | (t >> 5);  // bits 0..5: c0 | c1 << 3; bits 16..21: c2 | c3 << 3
+  return (v & 0x3Fu) | ((v >> 10) & 0xFC0u);
+}
+
+template <int kVariant = kMain>
 __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store) {
-  const uint32_t tid = threadIdx.x;
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t first = tile * kEncTileBf16;
   const bool tile_full = first + kEncTileBf16 <= a.n;  // same in every thread
   const uint4* w = in.w;
@@ -436,18 +459,43 @@ __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t ti
     r.mask[g] = f;
     cnt[g] = __builtin_popcount(f);
     if (store) {
-      const uint32_t nib = pack_codes8(lo, hi);
       // sign|mantissa: high bytes and low bytes of the four BF16 pairs
       const uint32_t h01 = perm(x.y, x.x, 0x07050301u), l01 = perm(x.y, x.x, 0x06040200u);
       const uint32_t h23 = perm(x.w, x.z, 0x07050301u), l23 = perm(x.w, x.z, 0x06040200u);
       const uint32_t sm0 = (h01 & 0x80808080u) | (l01 & 0x7F7F7F7Fu);
       const uint32_t sm1 = (h23 & 0x80808080u) | (l23 & 0x7F7F7F7Fu);
+      if (kVariant == kTop8) {
+        // 8 codes of 3 bits, element j at bit 3j: 3 bytes per thread, gathered
+        // per wave in LDS for 12 aligned 16-byte stores (in-order LDS within
+        // a wave: only the compiler needs a barrier)
+        const uint32_t c24 = codes12(lo) | (codes12(hi) << 12);
+        if (tile_full) {
+          uint8_t* buf = reinterpret_cast<uint8_t*>(sh.s3 + wave * 96);
+          buf[3 * lane] = (uint8_t)c24;
+          buf[3 * lane + 1] = (uint8_t)(c24 >> 8);
+          buf[3 * lane + 2] = (uint8_t)(c24 >> 16);
+          asm volatile("" ::: "memory");
+          if (lane < 12)
+            store_stream(a.out + a.nib + 3 * ((first + g * 2048 + 512 * wave) / 8) + 16 * lane,
+                         *reinterpret_cast<const uint4*>(sh.s3 + wave * 96 + 4 * lane));
+          asm volatile("" ::: "memory");
+        } else if (valid > 0) {
+          const uint64_t e0 = first + local;
+          for (uint32_t b = 0; b < 3 * ((valid + 7) / 8); ++b) a.out[a.nib + 3 * (e0 / 8) + b] = (uint8_t)(c24 >> (8 * b));
+        }
+      } else {
+        const uint32_t nib = pack_codes8(lo, hi);
+        if (tile_full) {
+          store_stream(a.out + a.nib + first / 2 + local / 2, nib);
+        } else if (valid > 0) {
+          const uint64_t e0 = first + local;
+          for (uint32_t b = 0; b < (valid + 1) / 2; ++b) a.out[a.nib + e0 / 2 + b] = (uint8_t)(nib >> (8 * b));
+        }
+      }
       if (tile_full) {
-        store_stream(a.out + a.nib + first / 2 + local / 2, nib);
         store_stream(a.out + a.sm + first + local, make_uint2(sm0, sm1));
       } else if (valid > 0) {
         const uint64_t e0 = first + local;
-        for (uint32_t b = 0; b < (valid + 1) / 2; ++b) a.out[a.nib + e0 / 2 + b] = (uint8_t)(nib >> (8 * b));
         for (uint32_t j = 0; j < valid; ++j) a.out[a.sm + e0 + j] = (uint8_t)((j < 4 ? sm0 : sm1) >> (8 * (j & 3)));
       }
     }
@@ -584,21 +632,27 @@ __device__ inline void for_each_escape_e5m2(const EncArgs& a, uint64_t tile, con
   }
 }
 
+template <int kVariant = kMain>
 __device__ inline void put_record(const EncArgs& a, uint64_t index, uint32_t pos, uint32_t val) {
   if (index >= a.n) return;  // never taken for a correct scan; keeps stores inside the stream
+  if (kVariant == kSentinel) {  // the raw exponent only
+    a.out[a.esc + index] = (uint8_t)val;
+    return;
+  }
   uint8_t* d = a.out + a.esc + 3 * index;
   d[0] = (uint8_t)pos;
   d[1] = (uint8_t)(pos >> 8);
   d[2] = (uint8_t)val;
 }
 
-template <bool kBf16>
+template <bool kBf16, int kVariant = kMain>
 __device__ void encode_dense(const EncArgs& a) {
   __shared__ EncShared sh;
   const uint64_t t = blockIdx.x;
   const TileIn in = kBf16 ? load_tile_bf16(a, t) : load_tile_e5m2(a, t);  // in flight during the table build
-  build_table(a, sh, a.seg_chunks ? codebook_of_chunk(t >> (kBf16 ? 3 : 2), a.seg_chunks) : 0, kBf16 ? 256u : 32u);
-  const TileEsc r = kBf16 ? encode_tile_bf16(a, sh, t, in, true) : encode_tile_e5m2(a, sh, t, in, true);
+  build_table<kVariant>(a, sh, a.seg_chunks ? codebook_of_chunk(t >> (kBf16 ? 3 : 2), a.seg_chunks) : 0,
+                        kBf16 ? 256u : 32u);
+  const TileEsc r = kBf16 ? encode_tile_bf16<kVariant>(a, sh, t, in, true) : encode_tile_e5m2(a, sh, t, in, true);
   if (threadIdx.x == 0) a.tile_count[t] = r.agg;
   if (r.agg <= kStageSlot) {  // uniform
     // records gathered in LDS first (the E5M2 tables are dead after the
@@ -616,6 +670,8 @@ __device__ void encode_dense(const EncArgs& a) {
 
 __global__ __launch_bounds__(kThreads) void encode_dense_bf16_kernel(EncArgs a) { encode_dense<true>(a); }
 __global__ __launch_bounds__(kThreads) void encode_dense_e5m2_kernel(EncArgs a) { encode_dense<false>(a); }
+__global__ __launch_bounds__(kThreads) void encode_dense_sentinel_kernel(EncArgs a) { encode_dense<true, kSentinel>(a); }
+__global__ __launch_bounds__(kThreads) void encode_dense_top8_kernel(EncArgs a) { encode_dense<true, kTop8>(a); }
 
 // One thread per block of 64 tiles, one wave per 64 blocks (a super-block):
 // block sums, and each wave's total as its super-block sum.
@@ -648,8 +704,9 @@ __global__ __launch_bounds__(kThreads) void encode_sums_kernel(EncArgs a) {
 
 constexpr uint32_t kPlaceBatch = 8;  // staged records per thread and step (loads issued together)
 
-template <bool kBf16>
+template <bool kBf16, int kVariant = kMain>
 __device__ void encode_place(const EncArgs& a) {
+  constexpr uint64_t kRec = kVariant == kSentinel ? 1 : 3;  // stream bytes per escape
   __shared__ PlaceShared sh;
   __shared__ EncShared esh;
   const uint32_t tid = threadIdx.x;
@@ -694,7 +751,7 @@ __device__ void encode_place(const EncArgs& a) {
     if (!staged) atomicOr(&sh.overflow, 1u);
     if (t == a.n_tiles - 1) {
       const uint64_t e = std::min<uint64_t>(base + pre + cnt, a.n);
-      const uint64_t s = a.esc + 3 * e;
+      const uint64_t s = a.esc + kRec * e;
       put_le(a.out + a.offsets + 8 * a.chunks, e, 8);
       put_le(a.out + 16, e, 8);
       put_le(a.out + 24, s, 8);
@@ -727,7 +784,7 @@ __device__ void encode_place(const EncArgs& a) {
     }
 #pragma unroll
     for (uint32_t u = 0; u < kPlaceBatch; ++u)
-      if (dst[u] != ~0ull) put_record(a, dst[u], v[u] & 0xFFFF, v[u] >> 16);
+      if (dst[u] != ~0ull) put_record<kVariant>(a, dst[u], v[u] & 0xFFFF, v[u] >> 16);
   }
   if (!sh.overflow) return;  // uniform
 
@@ -739,13 +796,13 @@ __device__ void encode_place(const EncArgs& a) {
     const uint64_t tt = blk * kBlockTiles + i;
     const uint64_t cbi = a.seg_chunks ? codebook_of_chunk(tt >> (kBf16 ? 3 : 2), a.seg_chunks) : 0;
     if (cbi != table_cb) {
-      build_table(a, esh, cbi, kBf16 ? 256u : 32u);
+      build_table<kVariant>(a, esh, cbi, kBf16 ? 256u : 32u);
       table_cb = cbi;
     }
     const TileIn in = kBf16 ? load_tile_bf16(a, tt) : load_tile_e5m2(a, tt);
-    const TileEsc r = kBf16 ? encode_tile_bf16(a, esh, tt, in, false) : encode_tile_e5m2(a, esh, tt, in, false);
+    const TileEsc r = kBf16 ? encode_tile_bf16<kVariant>(a, esh, tt, in, false) : encode_tile_e5m2(a, esh, tt, in, false);
     const uint64_t at = base + sh.pre_all[i];
-    auto direct = [&](uint32_t k, uint32_t pos, uint32_t val) { put_record(a, at + k, pos, val); };
+    auto direct = [&](uint32_t k, uint32_t pos, uint32_t val) { put_record<kVariant>(a, at + k, pos, val); };
     if (kBf16) for_each_escape_bf16(a, tt, r, direct);
     else for_each_escape_e5m2(a, tt, r, direct);
     __syncthreads();  // esh is reused by the next tile
@@ -754,6 +811,8 @@ __device__ void encode_place(const EncArgs& a) {
 
 __global__ __launch_bounds__(kThreads) void encode_place_bf16_kernel(EncArgs a) { encode_place<true>(a); }
 __global__ __launch_bounds__(kThreads) void encode_place_e5m2_kernel(EncArgs a) { encode_place<false>(a); }
+__global__ __launch_bounds__(kThreads) void encode_place_sentinel_kernel(EncArgs a) { encode_place<true, kSentinel>(a); }
+__global__ __launch_bounds__(kThreads) void encode_place_top8_kernel(EncArgs a) { encode_place<true, kTop8>(a); }
 
 // ---------------------------------------------------------- decode kernels
 struct DecArgs {
@@ -763,6 +822,7 @@ struct DecArgs {
   uint64_t n;
   int32_t* status;
   int dtype;
+  int variant;  // header byte 48
 };
 
 struct Header {
@@ -781,7 +841,7 @@ __device__ bool read_header(const DecArgs& a, Header& h) {
   if (w0 != kMagic) return false;
   if ((w1 & 0xFFFF) != 1 || ((w1 >> 16) & 0xFF) != (uint32_t)a.dtype || (w1 >> 24) != 16) return false;
   if (ld64(in + 8) != a.n) return false;
-  if (ld64(in + 48) != 0 || ld64(in + 56) != 0) return false;
+  if (ld64(in + 48) != (uint64_t)a.variant || ld64(in + 56) != 0) return false;  // variant byte, then zeros
   h.e = ld64(in + 16);
   const uint64_t total = ld64(in + 24);
   h.chunks = ld32(in + 32);
@@ -795,8 +855,8 @@ __device__ bool read_header(const DecArgs& a, Header& h) {
     return false;
   }
   if (h.e > a.n) return false;
-  h.s = sections_of(a.dtype, a.n, h.k);
-  if (total != h.s.esc + 3 * h.e || total > a.in_bytes) return false;
+  h.s = sections_of(a.dtype, a.n, h.k, a.variant);
+  if (total != h.s.esc + h.s.rec * h.e || total > a.in_bytes) return false;
   return true;
 }
 
@@ -1165,6 +1225,244 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
   }
 }
 
+// ---------------------------------------------- ablation decoders (BF16)
+// Top-8: 3-bit codes, 8 per 3 bytes, element j of a group at bit 3j; the
+// rest as the BF16 decode (8192-element tiles, 4 groups of 2048, 8 elements
+// per thread, escapes staged from the position records).
+__device__ inline uint32_t top8_spread4(uint32_t c12) {  // 4 codes of 3 bits -> one per byte
+  const uint32_t y = (c12 & 0x3Fu) | ((c12 << 10) & 0x3F0000u);
+  return (y & 0x00070007u) | ((y << 5) & 0x07000700u);
+}
+
+__device__ inline uint4 top8_decode8(uint32_t l0, uint32_t l1, uint32_t c24, uint2 sm) {
+  const uint32_t e_lo = perm(l1, l0, top8_spread4(c24 & 0xFFFu));  // exponents of elements 0..3
+  const uint32_t e_hi = perm(l1, l0, top8_spread4((c24 >> 12) & 0xFFFu));
+  const uint32_t m0 = sm.x & 0x7F7F7F7Fu, s0 = sm.x & 0x80808080u;
+  const uint32_t m1 = sm.y & 0x7F7F7F7Fu, s1 = sm.y & 0x80808080u;
+  // value pair (2k, 2k+1): mantissas and signs by one permute, exponents e << 7 and e << 23
+  return make_uint4(perm(s0, m0, 0x05010400u) | (perm(0u, e_lo, 0x0C010C00u) << 7),
+                    perm(s0, m0, 0x07030602u) | (perm(0u, e_lo, 0x0C030C02u) << 7),
+                    perm(s1, m1, 0x05010400u) | (perm(0u, e_hi, 0x0C010C00u) << 7),
+                    perm(s1, m1, 0x07030602u) | (perm(0u, e_hi, 0x0C030C02u) << 7));
+}
+
+__global__ __launch_bounds__(kThreads) void decode_top8_kernel(DecArgs a) {
+  constexpr uint32_t kDecTile = 8192, kGroups = 4;
+  __shared__ uint32_t bitmap[kDecTile / 32];
+  __shared__ alignas(16) uint8_t vals[kDecTile];
+  __shared__ uint32_t s_range[2];
+  __shared__ int s_err;
+  Header h;
+  if (!read_header(a, h)) {
+    if (threadIdx.x == 0) report_corrupt(a.status);
+    return;
+  }
+  if (a.n == 0) {
+    if (threadIdx.x == 0 && ld64(a.in + h.s.offsets) != 0) report_corrupt(a.status);
+    return;
+  }
+  const uint64_t tile = blockIdx.x;
+  const uint64_t chunk = tile / (kChunk / kDecTile);
+  const uint64_t cbi = h.k == 1 ? 0 : codebook_of_chunk(chunk, h.seg / kChunk);
+  const uint8_t* cb = a.in + 64 + 16 * cbi;
+  const uint32_t tid = threadIdx.x;
+  const uint64_t first = tile * kDecTile;
+  const bool fast = first + kDecTile <= a.n;  // same in every thread
+  const uint8_t* code_t = a.in + h.s.nib + 3 * (first / 8);
+  const uint8_t* sm_t = a.in + h.s.sm + first;
+  // the 3 code bytes of a thread lie in two aligned dwords; the last
+  // thread's second dword reaches 4 bytes past the tile's codes, still
+  // inside the stream (the sign|mantissa section follows)
+  uint32_t p0[kGroups], p1[kGroups];
+  uint2 sms[kGroups];
+  if (fast) {
+#pragma unroll
+    for (uint32_t g = 0; g < kGroups; ++g) {
+      const uint8_t* c = code_t + g * 768 + ((3 * tid) & ~3u);
+      p0[g] = ld32(c);
+      p1[g] = ld32(c + 4);
+      sms[g] = *reinterpret_cast<const uint2*>(sm_t + g * 2048 + 8 * tid);
+    }
+  }
+  const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4);
+  if (!stage_escapes<kDecTile>(a, h, tile, bitmap, vals, s_range, &s_err)) {
+    if (threadIdx.x == 0) report_corrupt(a.status);
+    return;
+  }
+  const uint8_t* bm8 = reinterpret_cast<const uint8_t*>(bitmap);
+  if (fast) {
+    uint8_t* out_t = a.out + 2 * first;
+    const uint32_t sh = 8 * ((3 * tid) & 3u);
+#pragma unroll
+    for (uint32_t g = 0; g < kGroups; ++g) {
+      const uint32_t local = g * 2048 + 8 * tid;
+      const uint32_t c24 = (uint32_t)(((((uint64_t)p1[g]) << 32) | p0[g]) >> sh) & 0xFFFFFFu;
+      uint4 o = top8_decode8(l0, l1, c24, sms[g]);
+      const uint32_t esc8 = bm8[local >> 3];
+      if (esc8) bf16_patch8(o, esc8, *reinterpret_cast<const uint2*>(vals + local));
+      store_stream(out_t + 2 * local, o);
+    }
+    return;
+  }
+  uint16_t* out16 = reinterpret_cast<uint16_t*>(a.out);
+#pragma unroll 1
+  for (uint32_t g = 0; g < kGroups; ++g) {
+    const uint32_t local = g * 2048 + 8 * tid;
+    const uint64_t e0 = first + local;
+    if (e0 >= a.n) break;
+    const uint32_t valid = (uint32_t)std::min<uint64_t>(8, a.n - e0);
+    uint32_t c24 = 0, t0 = 0, t1 = 0;
+    for (uint32_t b = 0; b < 3; ++b) c24 |= (uint32_t)code_t[3 * (local / 8) + b] << (8 * b);
+    for (uint32_t j = 0; j < valid; ++j) {
+      const uint32_t x = (uint32_t)sm_t[local + j] << (8 * (j & 3));
+      if (j < 4) t0 |= x;
+      else t1 |= x;
+    }
+    uint4 o = top8_decode8(l0, l1, c24, make_uint2(t0, t1));
+    const uint32_t esc8 = bm8[local >> 3];
+    if (esc8) bf16_patch8(o, esc8, *reinterpret_cast<const uint2*>(vals + local));
+    for (uint32_t j = 0; j < valid; ++j) out16[e0 + j] = (uint16_t)(pick4(o.x, o.y, o.z, o.w, j >> 1) >> (16 * (j & 1)));
+  }
+}
+
+// Sets the exponent field of value j (0..7) of a decoded group to v.
+__device__ inline void bf16_set_exponent(uint4& o, uint32_t j, uint32_t v) {
+  const uint32_t sh = (j & 1u) ? 23u : 7u;
+  const uint32_t m = 0xFFu << sh, x = v << sh;
+  switch (j >> 1) {
+    case 0: o.x = (o.x & ~m) | x; break;
+    case 1: o.y = (o.y & ~m) | x; break;
+    case 2: o.z = (o.z & ~m) | x; break;
+    default: o.w = (o.w & ~m) | x; break;
+  }
+}
+
+// Top-15 + sentinel: one workgroup per chunk.  A sentinel's raw exponent is
+// the next unread value of the chunk's list, so an element's value index is
+// the number of sentinels before it in the chunk: the chunk is decoded in 8
+// passes of 8192 elements, each with a workgroup scan of the threads'
+// sentinel counts, carried into the next pass.  This serial dependence is
+// what the pages avoid by storing positions.
+__global__ __launch_bounds__(kThreads) void decode_sentinel_kernel(DecArgs a) {
+  __shared__ uint32_t tab2[256];
+  __shared__ uint32_t wsum[2][8];
+  __shared__ int s_bad;
+  Header h;
+  if (!read_header(a, h)) {
+    if (threadIdx.x == 0) report_corrupt(a.status);
+    return;
+  }
+  if (a.n == 0) {
+    if (threadIdx.x == 0 && ld64(a.in + h.s.offsets) != 0) report_corrupt(a.status);
+    return;
+  }
+  const uint32_t tid = threadIdx.x, wave = tid >> 6;
+  const uint64_t chunk = blockIdx.x;
+  const uint64_t chunk_first = chunk * kChunk;
+  const uint32_t chunk_len = (uint32_t)std::min<uint64_t>(kChunk, a.n - chunk_first);
+  const uint64_t cbi = h.k == 1 ? 0 : codebook_of_chunk(chunk, h.seg / kChunk);
+  const uint8_t* cb = a.in + 64 + 16 * cbi;
+  const uint8_t* offs = a.in + h.s.offsets;
+  const uint64_t lo = ld64(offs + 8 * chunk), hi = ld64(offs + 8 * (chunk + 1));
+  bool ok = lo <= hi && hi <= h.e;
+  if (chunk == 0 && lo != 0) ok = false;
+  if (chunk == h.chunks - 1 && hi != h.e) ok = false;
+  if (!ok) {  // uniform
+    if (tid == 0) report_corrupt(a.status);
+    return;
+  }
+  {
+    const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4), l2 = ld32(cb + 8), l3 = ld32(cb + 12);
+    const uint32_t pair = lut4((tid & 0xFu) | ((tid >> 4) << 8), l0, l1, l2, l3);
+    tab2[tid] = ((pair & 0xFFu) << 7) | (((pair >> 8) & 0xFFu) << 23);
+  }
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  const uint8_t* nib_c = a.in + h.s.nib + chunk_first / 2;
+  const uint8_t* sm_c = a.in + h.s.sm + chunk_first;
+  const uint8_t* esc = a.in + h.s.esc;
+  uint16_t* out_c = reinterpret_cast<uint16_t*>(a.out) + chunk_first;
+  uint64_t run = lo;  // value index of the pass's first sentinel, same in every thread
+  bool bad = false;
+  for (uint32_t pass = 0; pass < kChunk / 8192; ++pass) {
+    const uint32_t pfirst = pass * 8192;
+    if (pfirst >= chunk_len) break;  // uniform
+    const bool full = pfirst + 8192 <= chunk_len;
+    uint32_t nibs[4], mk[4], cnt[4];
+    uint2 sms[4];
+#pragma unroll
+    for (uint32_t g = 0; g < 4; ++g) {
+      const uint32_t local = pfirst + g * 2048 + 8 * tid;
+      if (full) {
+        nibs[g] = ld32(nib_c + local / 2);
+        sms[g] = *reinterpret_cast<const uint2*>(sm_c + local);
+      } else {
+        const uint32_t valid = local < chunk_len ? std::min<uint32_t>(8, chunk_len - local) : 0u;
+        uint32_t tn = 0, t0 = 0, t1 = 0;
+        for (uint32_t j = 0; j < valid; ++j) {
+          const uint32_t nb = (nib_c[(local + j) / 2] >> (4 * (j & 1))) & 0xFu;  // missing elements: code 0
+          tn |= nb << (4 * j);
+          const uint32_t x = (uint32_t)sm_c[local + j] << (8 * (j & 3));
+          if (j < 4) t0 |= x;
+          else t1 |= x;
+        }
+        nibs[g] = tn;
+        sms[g] = make_uint2(t0, t1);
+      }
+      const uint32_t w = nibs[g];
+      mk[g] = w & (w >> 1) & (w >> 2) & (w >> 3) & 0x11111111u;  // nibble j == 15 -> bit 4j
+      cnt[g] = __builtin_popcount(mk[g]);
+    }
+    // element-order ranks within the pass: groups in order, threads in order
+    const uint32_t p01 = cnt[0] | (cnt[1] << 16), p23 = cnt[2] | (cnt[3] << 16);
+    const uint32_t i01 = wave_inclusive_sum(p01), i23 = wave_inclusive_sum(p23);
+    uint32_t* ws = wsum[pass & 1];
+    if ((tid & 63) == 63) {
+      ws[wave] = i01;
+      ws[4 + wave] = i23;
+    }
+    __syncthreads();
+    uint32_t pre01 = 0, pre23 = 0, tot01 = 0, tot23 = 0;
+#pragma unroll
+    for (uint32_t v = 0; v < 4; ++v) {
+      pre01 += v < wave ? ws[v] : 0u;
+      pre23 += v < wave ? ws[4 + v] : 0u;
+      tot01 += ws[v];
+      tot23 += ws[4 + v];
+    }
+    const uint32_t g0 = tot01 & 0xFFFF, g1 = tot01 >> 16, g2 = tot23 & 0xFFFF, g3 = tot23 >> 16;
+    const uint32_t x01 = pre01 + i01 - p01, x23 = pre23 + i23 - p23;
+    const uint32_t rank[4] = {x01 & 0xFFFF, g0 + (x01 >> 16), g0 + g1 + (x23 & 0xFFFF), g0 + g1 + g2 + (x23 >> 16)};
+#pragma unroll
+    for (uint32_t g = 0; g < 4; ++g) {
+      const uint32_t local = pfirst + g * 2048 + 8 * tid;
+      uint4 o = bf16_decode8(tab2, nibs[g], sms[g]);
+      uint32_t m = mk[g];
+      uint64_t idx = run + rank[g];
+      while (m) {  // sentinels: their raw exponents, in order
+        const uint32_t j = __builtin_ctz(m) >> 2;
+        m &= m - 1;
+        if (idx >= hi) {
+          bad = true;
+          break;
+        }
+        bf16_set_exponent(o, j, esc[idx]);
+        ++idx;
+      }
+      if (full) {
+        store_stream(out_c + local, o);
+      } else if (local < chunk_len) {
+        const uint32_t valid = std::min<uint32_t>(8, chunk_len - local);
+        for (uint32_t j = 0; j < valid; ++j) out_c[local + j] = (uint16_t)(pick4(o.x, o.y, o.z, o.w, j >> 1) >> (16 * (j & 1)));
+      }
+    }
+    run += g0 + g1 + g2 + g3;
+  }
+  if (bad) s_bad = 1;
+  __syncthreads();
+  if (tid == 0 && (s_bad || run != hi)) report_corrupt(a.status);
+}
+
 // ------------------------------------------------------------ host helpers
 bool dtype_valid(int dtype) { return dtype == SPLITZIP_BF16 || dtype == SPLITZIP_FP8_E5M2; }
 
@@ -1188,6 +1486,12 @@ int codebooks_valid(int dtype, const uint8_t* cbs, uint32_t k) {
   return 1;
 }
 
+// Worst-case stream plus encoder workspace.
+size_t max_size_of(int dtype, int variant, size_t n_elems, uint32_t n_codebooks) {
+  if (!dtype_valid(dtype) || n_codebooks == 0 || n_codebooks > kMaxK || n_elems > kMaxN) return 0;
+  return workspace_of(nullptr, dtype, n_elems, n_codebooks, variant).end;
+}
+
 }  // namespace
 
 // ================================================================== C ABI
@@ -1208,12 +1512,16 @@ int splitzip_calibrate(int dtype, const void* host_samples, size_t n_elems, uint
 
 size_t splitzip_max_compressed_size(int dtype, size_t n_elems, uint32_t n_codebooks) {
   if (!dtype_valid(dtype) || n_codebooks == 0 || n_codebooks > kMaxK || n_elems > kMaxN) return 0;
-  return workspace_of(nullptr, dtype, n_elems, n_codebooks).end;
+  return max_size_of(dtype, kMain, n_elems, n_codebooks);
 }
 
-int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks, uint32_t n_codebooks,
-                      size_t segment_elems, void* d_out, size_t out_capacity, uint64_t* d_out_bytes,
-                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int compress_impl(int dtype, int variant, const void* d_in, size_t n_elems, const uint8_t* h_codebooks,
+                  uint32_t n_codebooks, size_t segment_elems, void* d_out, size_t out_capacity, uint64_t* d_out_bytes,
+                  hipStream_t stream) {
   if (!dtype_valid(dtype) || n_elems > kMaxN || h_codebooks == nullptr || n_codebooks == 0 || n_codebooks > kMaxK)
     return SPLITZIP_E_INVALID;
   if ((d_in == nullptr && n_elems > 0) || d_out == nullptr || !aligned(d_in, 16) || !aligned(d_out, 16) ||
@@ -1222,13 +1530,13 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
   if (n_codebooks > 1 && (segment_elems == 0 || segment_elems % kChunk != 0 || segment_elems < divup(n_elems, n_codebooks)))
     return SPLITZIP_E_INVALID;
   if (!codebooks_valid(dtype, h_codebooks, n_codebooks)) return SPLITZIP_E_CODEBOOK;
-  if (out_capacity < splitzip_max_compressed_size(dtype, n_elems, n_codebooks)) return SPLITZIP_E_CAPACITY;
+  if (out_capacity < max_size_of(dtype, variant, n_elems, n_codebooks)) return SPLITZIP_E_CAPACITY;
 
   const uint64_t n = n_elems;
-  const Sections s = sections_of(dtype, n, n_codebooks);
+  const Sections s = sections_of(dtype, n, n_codebooks, variant);
   const uint64_t n_tiles = divup(n, dtype == SPLITZIP_BF16 ? kEncTileBf16 : kEncTileE5m2);
   uint8_t* out = static_cast<uint8_t*>(d_out);
-  const Workspace w = workspace_of(out, dtype, n, n_codebooks);
+  const Workspace w = workspace_of(out, dtype, n, n_codebooks, variant);
 
   for (uint32_t first = 0; first < n_codebooks; first += kCbPerPrep) {
     PrepArgs p;
@@ -1240,11 +1548,13 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
     p.sm = s.sm;
     p.esc = s.esc;
     p.sm_bytes = s.sm_bytes;
+    p.code_bytes = variant == kTop8 ? 3 * divup(n, 8) : divup(n, 2);
     p.offsets = s.offsets;
     p.chunks = s.chunks;
     p.out_bytes = d_out_bytes;
     p.k = n_codebooks;
     p.dtype = (uint32_t)dtype;
+    p.variant = (uint32_t)variant;
     p.cb_first = first;
     p.cb_count = std::min<uint32_t>(kCbPerPrep, n_codebooks - first);
     p.main = first == 0;
@@ -1274,15 +1584,43 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
   const uint32_t tiles = (uint32_t)n_tiles;  // n <= 2^40 -> at most 2^27 tiles
   const uint64_t blocks = divup(n_tiles, kBlockTiles);
   e.n_blocks = blocks;
-  if (dtype == SPLITZIP_BF16) encode_dense_bf16_kernel<<<tiles, kThreads, 0, stream>>>(e);
-  else encode_dense_e5m2_kernel<<<tiles, kThreads, 0, stream>>>(e);
+  if (dtype == SPLITZIP_FP8_E5M2) encode_dense_e5m2_kernel<<<tiles, kThreads, 0, stream>>>(e);
+  else if (variant == kSentinel) encode_dense_sentinel_kernel<<<tiles, kThreads, 0, stream>>>(e);
+  else if (variant == kTop8) encode_dense_top8_kernel<<<tiles, kThreads, 0, stream>>>(e);
+  else encode_dense_bf16_kernel<<<tiles, kThreads, 0, stream>>>(e);
   if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
   encode_sums_kernel<<<(uint32_t)divup(blocks, kThreads), kThreads, 0, stream>>>(e);
   if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
-  if (dtype == SPLITZIP_BF16) encode_place_bf16_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(e);
-  else encode_place_e5m2_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(e);
+  if (dtype == SPLITZIP_FP8_E5M2) encode_place_e5m2_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(e);
+  else if (variant == kSentinel) encode_place_sentinel_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(e);
+  else if (variant == kTop8) encode_place_top8_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(e);
+  else encode_place_bf16_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(e);
   if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
   return SPLITZIP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks, uint32_t n_codebooks,
+                      size_t segment_elems, void* d_out, size_t out_capacity, uint64_t* d_out_bytes,
+                      hipStream_t stream) {
+  return compress_impl(dtype, kMain, d_in, n_elems, h_codebooks, n_codebooks, segment_elems, d_out, out_capacity,
+                       d_out_bytes, stream);
+}
+
+size_t splitzip_variant_max_compressed_size(int variant, size_t n_elems, uint32_t n_codebooks) {
+  if (variant != kSentinel && variant != kTop8) return 0;
+  return max_size_of(SPLITZIP_BF16, variant, n_elems, n_codebooks);
+}
+
+int splitzip_variant_compress(int variant, const void* d_in, size_t n_elems, const uint8_t* h_codebooks,
+                              uint32_t n_codebooks, size_t segment_elems, void* d_out, size_t out_capacity,
+                              uint64_t* d_out_bytes, hipStream_t stream) {
+  if (variant != kSentinel && variant != kTop8) return SPLITZIP_E_INVALID;
+  return compress_impl(SPLITZIP_BF16, variant, d_in, n_elems, h_codebooks, n_codebooks, segment_elems, d_out,
+                       out_capacity, d_out_bytes, stream);
 }
 
 int splitzip_decompress(const void* d_in, size_t in_bytes, int dtype, size_t n_elems, void* d_out, int32_t* d_status,
@@ -1297,12 +1635,35 @@ int splitzip_decompress(const void* d_in, size_t in_bytes, int dtype, size_t n_e
   a.n = n_elems;
   a.status = d_status;
   a.dtype = dtype;
+  a.variant = kMain;
   // one workgroup per tile; a header-only stream (n == 0) still gets one
   // workgroup, which only validates
   if (dtype == SPLITZIP_BF16) {
     decode_bf16_kernel<<<(uint32_t)std::max<uint64_t>(1, divup(n_elems, kDecTileBf16)), kThreads, 0, stream>>>(a);
   } else {
     decode_e5m2_kernel<<<(uint32_t)std::max<uint64_t>(1, divup(n_elems, kDecTileE5m2)), kThreads, 0, stream>>>(a);
+  }
+  if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
+  return SPLITZIP_OK;
+}
+
+int splitzip_variant_decompress(int variant, const void* d_in, size_t in_bytes, size_t n_elems, void* d_out,
+                                int32_t* d_status, hipStream_t stream) {
+  if ((variant != kSentinel && variant != kTop8) || n_elems > kMaxN || d_in == nullptr || in_bytes < 64 ||
+      !aligned(d_in, 16) || (d_out == nullptr && n_elems > 0) || !aligned(d_out, 16) || !aligned(d_status, 4))
+    return SPLITZIP_E_INVALID;
+  DecArgs a;
+  a.in = static_cast<const uint8_t*>(d_in);
+  a.in_bytes = in_bytes;
+  a.out = static_cast<uint8_t*>(d_out);
+  a.n = n_elems;
+  a.status = d_status;
+  a.dtype = SPLITZIP_BF16;
+  a.variant = variant;
+  if (variant == kTop8) {
+    decode_top8_kernel<<<(uint32_t)std::max<uint64_t>(1, divup(n_elems, 8192)), kThreads, 0, stream>>>(a);
+  } else {
+    decode_sentinel_kernel<<<(uint32_t)std::max<uint64_t>(1, divup(n_elems, kChunk)), kThreads, 0, stream>>>(a);
   }
   if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
   return SPLITZIP_OK;

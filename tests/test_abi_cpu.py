@@ -133,3 +133,22 @@ def test_calibrate_device_work_bytes_and_argument_errors():
     ]
     for args, want in cases:
         assert sz.splitzip_calibrate_device(*args) == want, args
+
+
+def test_variant_max_size_and_argument_errors():
+    for v in (sz.VARIANT_TOP15_SENTINEL, sz.VARIANT_TOP8):
+        for n, k in [(0, 1), (1, 1), (8191, 1), (1 << 20, 4)]:
+            cap = sz.splitzip_variant_max_compressed_size(v, n, k)
+            assert cap >= O.variant_max_size(v, n, k) and cap % 256 == 0
+    assert sz.splitzip_variant_max_compressed_size(0, 100, 1) == 0
+    assert sz.splitzip_variant_max_compressed_size(3, 100, 1) == 0
+    lib = sz.load()
+    cb = np.arange(16, dtype=np.uint8)
+    p = 1 << 20
+    assert lib.splitzip_variant_compress(3, p, 100, cb.ctypes.data, 1, 0, p, 1 << 20, None, None) == sz.E_INVALID
+    assert lib.splitzip_variant_compress(1, p, 100, cb.ctypes.data, 1, 0, p, 100, None, None) == sz.E_CAPACITY
+    dup = cb.copy()
+    dup[3] = dup[4]
+    assert lib.splitzip_variant_compress(2, p, 100, dup.ctypes.data, 1, 0, p, 1 << 20, None, None) == sz.E_CODEBOOK
+    assert lib.splitzip_variant_decompress(0, p, 4096, 100, p, None, None) == sz.E_INVALID
+    assert lib.splitzip_variant_decompress(1, p, 32, 100, p, None, None) == sz.E_INVALID   # shorter than a header
