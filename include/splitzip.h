@@ -230,7 +230,8 @@ int splitzip_pipeline_sizes(int dtype, size_t n_elems, uint32_t n_codebooks, siz
  *   streams       four distinct streams: encode, device-to-host copies,
  *                 host-to-device copies, decode.
  * Blocking: the calling thread drives the pipeline and returns after all four
- * streams are synchronized.  On an error return, work already queued may
+ * streams are synchronized; if no step can proceed for 60 s it returns
+ * SPLITZIP_E_HIP.  On an error return, work already queued may
  * still run; synchronize the streams before reusing the buffers.  Returns
  * SPLITZIP_OK, SPLITZIP_E_INVALID, SPLITZIP_E_CAPACITY, SPLITZIP_E_CODEBOOK
  * or SPLITZIP_E_HIP. */

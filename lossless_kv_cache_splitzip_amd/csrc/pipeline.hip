@@ -20,6 +20,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <chrono>
 #include <thread>
 #include <vector>
 
@@ -135,6 +136,10 @@ int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, cons
   // next group to take each step: compress, copy out, copy back, decode
   uint64_t nc = 0, nd = 0, nh = 0, nx = 0;
   const uint64_t G = p.groups;
+  // a step that makes no progress for this long means the device stopped
+  // answering: give up rather than spin forever
+  constexpr auto kStall = std::chrono::seconds(60);
+  auto last_progress = std::chrono::steady_clock::now();
   while (compress ? nx < G : nh < G) {
     bool progress = false;
     // compress g: its send slot is free once group g - depth was copied out
@@ -191,7 +196,12 @@ int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, cons
       ++nx, progress = true;
     }
     if (qerr != hipSuccess) return SPLITZIP_E_HIP;
-    if (!progress) std::this_thread::yield();
+    if (progress) {
+      last_progress = std::chrono::steady_clock::now();
+    } else {
+      if (std::chrono::steady_clock::now() - last_progress > kStall) return SPLITZIP_E_HIP;
+      std::this_thread::yield();
+    }
   }
   for (int i = 0; i < 4; ++i)
     if (hipStreamSynchronize(streams[i]) != hipSuccess) return SPLITZIP_E_HIP;
