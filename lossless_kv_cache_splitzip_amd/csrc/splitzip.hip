@@ -962,19 +962,31 @@ __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, 
   __syncthreads();
   const uint64_t ra = lo + s_range[0], rb = lo + s_range[1];
   bool bad = false;
-  for (uint64_t r = ra + tid; r < rb; r += kThreads) {
-    const uint8_t* rec = a.in + h.s.esc + 3 * r;
-    const uint32_t pos = record_pos(rec);
-    const uint32_t v = rec[2];
-    const uint32_t local = pos - win_lo;  // wraps for pos < win_lo
-    bool good = pos >= win_lo && local < win_len && v < vmax;
-    if (good && r > ra) good = record_pos(rec - 3) < pos;
-    if (!good) {
-      bad = true;
-      continue;
+  // kScanRecs records per thread per step, their loads issued together
+  for (uint64_t r0 = ra; r0 < rb; r0 += (uint64_t)kScanRecs * kThreads) {
+    uint32_t pos[kScanRecs], prev1[kScanRecs], val[kScanRecs];
+#pragma unroll
+    for (uint32_t k = 0; k < kScanRecs; ++k) {
+      const uint64_t r = r0 + k * kThreads + tid;
+      pos[k] = ~0u;  // no record
+      if (r < rb) {
+        const uint8_t* rec = a.in + h.s.esc + 3 * r;
+        pos[k] = record_pos(rec);
+        val[k] = rec[2];
+        prev1[k] = r > ra ? record_pos(rec - 3) + 1 : 0;  // predecessor's position + 1, 0 for the first
+      }
     }
-    vals[local] = (uint8_t)v;
-    atomicOr(&bitmap[local >> 5], 1u << (local & 31));
+#pragma unroll
+    for (uint32_t k = 0; k < kScanRecs; ++k) {
+      if (pos[k] == ~0u) continue;
+      const uint32_t local = pos[k] - win_lo;  // wraps for pos < win_lo
+      if (pos[k] < win_lo || local >= win_len || val[k] >= vmax || prev1[k] > pos[k]) {
+        bad = true;
+        continue;
+      }
+      vals[local] = (uint8_t)val[k];
+      atomicOr(&bitmap[local >> 5], 1u << (local & 31));
+    }
   }
   if (bad) *s_err = 1;
   __syncthreads();
