@@ -80,14 +80,15 @@ SPECS = {
     "long_ctx_heavy_tail_bf16": Spec("long_ctx_heavy_tail_bf16", 3, BF16, 28, 32768, 4,
                                      sigma=math.sqrt(2.0), outlier_p=0.05, outlier_f=100.0,
                                      calib="sigma1"),
-    # Edge cases, 134,217,728 BF16 values (256 MiB) each, one codebook.
-    "edge_const_exponent": Spec("edge_const_exponent", 41, BF16, 1, 134217728 // 1024, 8,
+    # Edge cases, 134,217,728 BF16 values (256 MiB) each, one codebook:
+    # [1, 2, 65536, 8, 128].
+    "edge_const_exponent": Spec("edge_const_exponent", 41, BF16, 1, 65536, 8,
                                 kind="const_exponent", calib="same_generator",
                                 per_layer_codebooks=False),
-    "edge_uniform_bits": Spec("edge_uniform_bits", 42, BF16, 1, 134217728 // 1024, 8,
+    "edge_uniform_bits": Spec("edge_uniform_bits", 42, BF16, 1, 65536, 8,
                               kind="uniform_bits", calib="same_generator",
                               per_layer_codebooks=False),
-    "edge_special_values": Spec("edge_special_values", 43, BF16, 1, 134217728 // 1024, 8,
+    "edge_special_values": Spec("edge_special_values", 43, BF16, 1, 65536, 8,
                                 kind="special_mix", calib="same_generator",
                                 per_layer_codebooks=False),
     # FP8 E5M2, Llama-3-70B-shaped, one GPU's share: [80, 2, 16384, 8, 128].
