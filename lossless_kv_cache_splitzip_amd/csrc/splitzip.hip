@@ -20,8 +20,10 @@
 //                 stores, element-order escape ranks (wave64 DPP scan +
 //                 LDS), escape records staged per tile in the workspace.
 //   encode_sums   escape count of each block of 64 tiles.
-//   encode_place  per block: base (lower super-blocks and blocks), tile scan, chunk
-//                 offsets, staged records copied to their place.
+//   encode_place  per range of 8 to 64 tiles: base (lower super-blocks,
+//                 blocks and tiles), tile scan, chunk offsets, staged records
+//                 moved to their place through LDS (word stores); tiles whose
+//                 records overflowed their slot are encoded again.
 //   decode        one workgroup per tile inside one chunk (8192 BF16 or
 //                 16384 E5M2 elements).  Dense loads go out first; the
 //                 tile's escape records are staged in LDS (bitmap + values),
@@ -252,11 +254,12 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 //                 slot.
 //   encode_sums   one thread per block of kBlockTiles tiles: the block's
 //                 escape count.
-//   encode_place  one workgroup per block: block base = sum of the lower
-//                 blocks, scan of its tiles' counts, chunk offsets (E and S
-//                 for the last block), staged records copied to their place;
-//                 a tile whose escapes overflowed its slot is read again and
-//                 its records written directly.
+//   encode_place  one workgroup per range of 8 to 64 tiles (about 2048
+//                 workgroups): the range's base (sum of the lower blocks and
+//                 tiles), scan of its tiles' counts, chunk offsets (E and S
+//                 for the last range), staged records moved to their place;
+//                 a tile whose escapes overflowed its slot is encoded again.
+//                 Records reach the stream through LDS as whole words.
 struct EncArgs {
   const uint8_t* in;
   uint8_t* out;
@@ -267,6 +270,7 @@ struct EncArgs {
   uint64_t* block_sum;    // per block of kBlockTiles tiles: escapes in it
   uint64_t* super_sum;    // per 64 blocks: escapes in them
   uint64_t* out_bytes;
+  uint32_t place_tiles;   // tiles per encode_place workgroup: 8, 16, 32 or 64
 };
 
 constexpr uint32_t kStageSlot = 512;  // staged escape records per tile
@@ -286,11 +290,14 @@ struct EncShared {
 
 static_assert(kStageSlot <= 4 * 256, "staged records reuse the E5M2 table space");
 
+constexpr uint32_t kPlaceRecs = 2048;  // escape records per LDS window of encode_place
+constexpr uint32_t kPlaceWgs = 2048;   // encode_place aims at this many workgroups
+
 struct PlaceShared {
   uint64_t red[16];
-  uint32_t pre_all[kBlockTiles + 1];     // escapes before each tile of the block
-  uint32_t pre_staged[kBlockTiles + 1];  // staged records before each tile of the block
-  uint32_t overflow;                     // some tile of the block is not staged
+  uint32_t pre_all[kBlockTiles + 1];     // escapes before each tile of the range
+  uint32_t pre_staged[kBlockTiles + 1];  // staged records before each tile of the range
+  alignas(16) uint32_t rec[kPlaceRecs];  // re-encoded tile's records (position | exponent << 16) in escape order
 };
 
 // Exclusive prefix over the workgroup's threads (thread order) of per-thread
@@ -316,10 +323,10 @@ __device__ inline uint32_t block_exclusive_sum(uint64_t* red, uint32_t v, uint32
 // code, every other exponent the escape entry (kEsc; with the sentinel
 // variant kEsc | 15, so an escape's nibble is the sentinel).
 template <int kVariant = kMain>
-__device__ inline void build_table(const EncArgs& a, EncShared& sh, uint64_t cbi, uint32_t entries) {
+__device__ inline void build_table(const EncArgs& a, EncShared& sh, uint64_t cbi, uint32_t entries,
+                                   uint32_t tid = threadIdx.x) {
   constexpr uint32_t kCodes = kVariant == kSentinel ? 15 : kVariant == kTop8 ? 8 : 16;
   constexpr uint8_t kEscEntry = kVariant == kSentinel ? (kEsc | 15) : kEsc;
-  const uint32_t tid = threadIdx.x;
   if (tid < entries) sh.table[tid] = kEscEntry;
   __syncthreads();
   if (tid < kCodes) sh.table[a.out[64 + 16 * cbi + tid]] = (uint8_t)tid;
@@ -343,9 +350,9 @@ struct TileEsc {
   uint32_t mask[4];  // escaped elements of each group, bit j = element j
 };
 
-__device__ inline void wave_totals_to_lds(EncShared& sh, uint32_t i01, uint32_t i23) {
-  const uint32_t wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 63) {
+__device__ inline void wave_totals_to_lds(EncShared& sh, uint32_t i01, uint32_t i23, uint32_t tid) {
+  const uint32_t wave = tid >> 6;
+  if ((tid & 63) == 63) {
     sh.wave[wave] = i01;
     sh.wave[4 + wave] = i23;
   }
@@ -355,11 +362,11 @@ __device__ inline void wave_totals_to_lds(EncShared& sh, uint32_t i01, uint32_t 
 // Element-order ranks of a tile of four groups: groups are ordered (g,
 // thread), so the four per-thread counts are scanned as 16-bit fields (a
 // group holds at most 4096 escapes).
-__device__ inline void tile_ranks4(EncShared& sh, const uint32_t cnt[4], TileEsc& r) {
-  const uint32_t wave = threadIdx.x >> 6;
+__device__ inline void tile_ranks4(EncShared& sh, const uint32_t cnt[4], TileEsc& r, uint32_t tid) {
+  const uint32_t wave = tid >> 6;
   const uint32_t p01 = cnt[0] | (cnt[1] << 16), p23 = cnt[2] | (cnt[3] << 16);
   const uint32_t i01 = wave_inclusive_sum(p01), i23 = wave_inclusive_sum(p23);
-  wave_totals_to_lds(sh, i01, i23);
+  wave_totals_to_lds(sh, i01, i23, tid);
   uint32_t pre01 = 0, pre23 = 0, tot01 = 0, tot23 = 0;
 #pragma unroll
   for (uint32_t v = 0; v < 4; ++v) {
@@ -389,8 +396,7 @@ __device__ inline uint32_t valid_in_group(uint64_t n, uint64_t e0, uint32_t widt
   return e0 >= n ? 0u : (uint32_t)std::min<uint64_t>(width, n - e0);
 }
 
-__device__ inline TileIn load_tile_bf16(const EncArgs& a, uint64_t tile) {
-  const uint32_t tid = threadIdx.x;
+__device__ inline TileIn load_tile_bf16(const EncArgs& a, uint64_t tile, uint32_t tid = threadIdx.x) {
   const uint64_t first = tile * kEncTileBf16;
   const uint16_t* src = reinterpret_cast<const uint16_t*>(a.in) + first;
   TileIn in;
@@ -434,8 +440,9 @@ __device__ inline uint32_t codes12(uint32_t w) {
 }
 
 template <int kVariant = kMain>
-__device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store) {
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store,
+                                   uint32_t tid = threadIdx.x) {
+  const uint32_t lane = tid & 63, wave = tid >> 6;
   const uint64_t first = tile * kEncTileBf16;
   const bool tile_full = first + kEncTileBf16 <= a.n;  // same in every thread
   const uint4* w = in.w;
@@ -500,15 +507,25 @@ __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t ti
       }
     }
   }
-  tile_ranks4(sh, cnt, r);
+  tile_ranks4(sh, cnt, r, tid);
   return r;
 }
 
 // The escapes of one BF16 tile: position in chunk and raw exponent, handed
-// to `put(rank, pos, exponent)` in element order.
-template <typename Put>
-__device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put) {
-  const uint32_t tid = threadIdx.x;
+// to `put(rank, pos, exponent)` in element order.  The exponent is read again
+// from the input, or, when `in` is given, taken from the tile's registers
+// (the dense kernel reads it again: keeping the input registers live there
+// measured slower; the re-encode of an escape-heavy tile takes it from
+// registers).  With kWindow, only ranks in [w0, w0 + wlen) are wanted: a
+// thread's escapes of one group have consecutive ranks, and groups whose
+// ranks all miss the window are skipped.
+__device__ inline bool ranks_miss(uint32_t k, uint32_t count, uint32_t w0, uint32_t wlen) {
+  return k + count <= w0 || (k >= w0 && k - w0 >= wlen);
+}
+
+template <bool kWindow = false, typename Put>
+__device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put,
+                                            uint32_t w0 = 0, uint32_t wlen = 0, uint32_t tid = threadIdx.x, const TileIn* in = nullptr) {
   const uint16_t* in16 = reinterpret_cast<const uint16_t*>(a.in);
   const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTileBf16;
 #pragma unroll
@@ -516,11 +533,13 @@ __device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, con
     const uint32_t f = r.mask[g];  // element k at bit 8k, element 4 + k at bit 8k + 1
     uint32_t m = f ? flag_mask4(f << 4) | (flag_mask4(f << 3) << 4) : 0u;  // element order
     uint32_t k = r.rank[g];
+    if (kWindow && ranks_miss(k, __builtin_popcount(m), w0, wlen)) continue;
     const uint64_t e0 = tile * kEncTileBf16 + g * 2048 + 8 * tid;
     while (m) {
       const uint32_t j = __builtin_ctz(m);
       m &= m - 1;
-      put(k++, in_chunk + g * 2048 + 8 * tid + j, (uint32_t)(in16[e0 + j] >> 7) & 0xFF);
+      const uint32_t x = in ? pick4(in->w[g].x, in->w[g].y, in->w[g].z, in->w[g].w, j >> 1) >> (16 * (j & 1)) : in16[e0 + j];
+      put(k++, in_chunk + g * 2048 + 8 * tid + j, (x >> 7) & 0xFF);
     }
   }
 }
@@ -528,9 +547,8 @@ __device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, con
 // E5M2 tile: 16384 elements = 4 groups of 4096; thread t owns elements
 // 16t..16t+15 of each group: 16 input bytes, 8 nibble bytes and 6
 // sign|mantissa bytes, all lane-contiguous across a wave.
-__device__ inline TileIn load_tile_e5m2(const EncArgs& a, uint64_t tile) {
+__device__ inline TileIn load_tile_e5m2(const EncArgs& a, uint64_t tile, uint32_t tid = threadIdx.x) {
   TileIn in;
-  const uint32_t tid = threadIdx.x;
   const uint64_t first = tile * kEncTileE5m2;
   const uint8_t* src = a.in + first;
   if (first + kEncTileE5m2 <= a.n) {  // same in every thread
@@ -558,8 +576,9 @@ __device__ inline uint32_t e5m2_pos_word(const uint32_t* pos4, uint32_t x) {
   return pos4[x & 0xFFu] | pos4[256 + ((x >> 8) & 0xFFu)] | pos4[512 + ((x >> 16) & 0xFFu)] | pos4[768 + (x >> 24)];
 }
 
-__device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store) {
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store,
+                                   uint32_t tid = threadIdx.x) {
+  const uint32_t lane = tid & 63, wave = tid >> 6;
   const uint64_t first = tile * kEncTileE5m2;
   const bool tile_full = first + kEncTileE5m2 <= a.n;  // same in every thread
   TileEsc r;
@@ -611,23 +630,25 @@ __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t ti
         a.out[smo + b] = (uint8_t)((b < 4 ? lo : hi) >> (8 * (b & 3)));
     }
   }
-  tile_ranks4(sh, cnt, r);
+  tile_ranks4(sh, cnt, r, tid);
   return r;
 }
 
-template <typename Put>
-__device__ inline void for_each_escape_e5m2(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put) {
-  const uint32_t tid = threadIdx.x;
+template <bool kWindow = false, typename Put>
+__device__ inline void for_each_escape_e5m2(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put,
+                                            uint32_t w0 = 0, uint32_t wlen = 0, uint32_t tid = threadIdx.x, const TileIn* in = nullptr) {
   const uint32_t in_chunk = (uint32_t)(tile & 3) * (uint32_t)kEncTileE5m2;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     uint32_t m = r.mask[g];
     uint32_t k = r.rank[g];
+    if (kWindow && ranks_miss(k, __builtin_popcount(m), w0, wlen)) continue;
     const uint64_t e0 = tile * kEncTileE5m2 + g * 4096 + 16 * tid;
     while (m) {
       const uint32_t j = __builtin_ctz(m);
       m &= m - 1;
-      put(k++, in_chunk + g * 4096 + 16 * tid + j, (uint32_t)(a.in[e0 + j] >> 2) & 0x1F);
+      const uint32_t x = in ? pick4(in->w[g].x, in->w[g].y, in->w[g].z, in->w[g].w, j >> 2) >> (8 * (j & 3)) : a.in[e0 + j];
+      put(k++, in_chunk + g * 4096 + 16 * tid + j, (x >> 2) & 0x1F);
     }
   }
 }
@@ -704,21 +725,66 @@ __global__ __launch_bounds__(kThreads) void encode_sums_kernel(EncArgs a) {
 
 constexpr uint32_t kPlaceBatch = 8;  // staged records per thread and step (loads issued together)
 
+// Records rec[0, m) (LDS, position | exponent << 16) to escape indices
+// [d0, d0 + m) of the stream.  Records whose index is a multiple of 4 start
+// on a 4-byte boundary (the escape section is 256-aligned), so every 4
+// records fill 3 whole words (1 with the sentinel variant) and are written
+// with word stores; the records before the first such index and after the
+// last group are written byte by byte.  Other workgroups may write the
+// neighbouring bytes of the first and last words: stores carry byte masks.
+template <int kVariant = kMain>
+__device__ void write_records(const EncArgs& a, const uint32_t* rec, uint64_t d0, uint32_t m, uint32_t tid = threadIdx.x) {
+  const uint32_t head = std::min<uint32_t>(m, (uint32_t)(-d0 & 3));
+  const uint32_t groups = (m - head) / 4, tail = head + 4 * groups;
+  if (tid < head) put_record<kVariant>(a, d0 + tid, rec[tid] & 0xFFFF, rec[tid] >> 16);
+  if (tid < m - tail) put_record<kVariant>(a, d0 + tail + tid, rec[tail + tid] & 0xFFFF, rec[tail + tid] >> 16);
+  for (uint32_t g = tid; g < groups; g += kThreads) {
+    const uint32_t* r = rec + head + 4 * g;
+    const uint32_t r0 = r[0], r1 = r[1], r2 = r[2], r3 = r[3];
+    const uint64_t idx = d0 + head + 4 * (uint64_t)g;
+    if (idx + 4 > a.n) continue;  // never taken for a correct scan; keeps stores inside the stream
+    if (kVariant == kSentinel) {  // exponent bytes only
+      *reinterpret_cast<uint32_t*>(a.out + a.esc + idx) = (r0 >> 16) | ((r1 >> 8) & 0xFF00u) | (r2 & 0xFF0000u) | (r3 << 8 & 0xFF000000u);
+    } else {  // 12 bytes: [pos lo, pos hi, exponent] x 4
+      uint32_t* d = reinterpret_cast<uint32_t*>(a.out + a.esc + 3 * idx);
+      d[0] = (r0 & 0xFFFFFFu) | (r1 << 24);
+      d[1] = ((r1 >> 8) & 0xFFFFu) | (r2 << 16);
+      d[2] = ((r2 >> 16) & 0xFFu) | (r3 << 8);
+    }
+  }
+}
+
+// One workgroup per range of place_tiles tiles (a power of two up to
+// kBlockTiles, so a range lies inside one block): the range's base (escapes
+// of the lower super-blocks, of the lower blocks of its super-block and of
+// the lower tiles of its block), the scan of its tiles' counts, its chunk
+// offsets (E, S and the stream size for the last range), its staged records
+// moved to their place, and its tiles whose escapes overflowed their slot
+// encoded again.
 template <bool kBf16, int kVariant = kMain>
 __device__ void encode_place(const EncArgs& a) {
   constexpr uint64_t kRec = kVariant == kSentinel ? 1 : 3;  // stream bytes per escape
   __shared__ PlaceShared sh;
   __shared__ EncShared esh;
   const uint32_t tid = threadIdx.x;
-  const uint64_t blk = blockIdx.x;
-  // block base: escapes of all lower blocks = the lower super-blocks plus the
-  // lower blocks of this super-block
-  uint64_t part = 0;
-  for (uint64_t i = tid; i < (blk >> 6); i += kThreads) part += a.super_sum[i];
-  if (tid < (blk & 63)) part += a.block_sum[(blk & ~63ull) + tid];
+  const uint64_t t0 = (uint64_t)blockIdx.x * a.place_tiles;
+  const uint32_t tiles = (uint32_t)std::min<uint64_t>(a.place_tiles, a.n_tiles - t0);
+  const uint64_t blk = t0 / kBlockTiles;
+  const uint32_t below = (uint32_t)(t0 % kBlockTiles);  // tiles of the block before the range
+  const uint64_t t = t0 + tid;
+  const bool mine = tid < tiles;
+  const uint32_t cnt = mine ? a.tile_count[t] : 0u;
+  const bool over = cnt > kStageSlot;
+
+  // base: the first wave adds the lower blocks of the super-block, the
+  // second the lower tiles of the block, all waves the lower super-blocks
+  uint64_t lower = 0;
+  for (uint64_t i = tid; i < (blk >> 6); i += kThreads) lower += a.super_sum[i];
+  if (tid < (blk & 63)) lower += a.block_sum[(blk & ~63ull) + tid];
+  if (tid >= 64 && tid - 64 < below) lower += a.tile_count[blk * kBlockTiles + (tid - 64)];
   {
     // wave sum of u64 through two u32 halves; one lane per wave stores it
-    uint64_t v = part;
+    uint64_t v = lower;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
       const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
@@ -730,25 +796,19 @@ __device__ void encode_place(const EncArgs& a) {
   __syncthreads();
   const uint64_t base = sh.red[8] + sh.red[9] + sh.red[10] + sh.red[11];
 
-  // this block's tiles (one per thread of the first wave): counts, in-block
-  // offsets, chunk offsets
-  const uint64_t t = blk * kBlockTiles + tid;
-  const bool mine = tid < kBlockTiles && t < a.n_tiles;
-  const uint32_t cnt = mine ? a.tile_count[t] : 0u;
-  const bool staged = cnt <= kStageSlot;
+  // in-range offsets of the tiles
   uint32_t total, staged_total;
   const uint32_t pre = block_exclusive_sum<kThreads / 64>(sh.red, cnt, &total);
-  const uint32_t spre = block_exclusive_sum<kThreads / 64>(sh.red, staged ? cnt : 0u, &staged_total);
+  const uint32_t spre = block_exclusive_sum<kThreads / 64>(sh.red, over ? 0u : cnt, &staged_total);
   if (tid <= kBlockTiles) {
     sh.pre_all[tid] = pre;
     sh.pre_staged[tid] = spre;
   }
-  if (tid == 0) sh.overflow = 0;
+  const bool any_over = staged_total != total;  // uniform
   __syncthreads();
   if (mine) {
     constexpr uint32_t kTpcLog2 = kBf16 ? 3 : 2;  // tiles per chunk: 8 BF16, 4 E5M2
     if ((t & ((1u << kTpcLog2) - 1)) == 0) put_le(a.out + a.offsets + 8 * (t >> kTpcLog2), base + pre, 8);
-    if (!staged) atomicOr(&sh.overflow, 1u);
     if (t == a.n_tiles - 1) {
       const uint64_t e = std::min<uint64_t>(base + pre + cnt, a.n);
       const uint64_t s = a.esc + kRec * e;
@@ -758,11 +818,9 @@ __device__ void encode_place(const EncArgs& a) {
       if (a.out_bytes) *a.out_bytes = s;
     }
   }
-  __syncthreads();
 
-  // staged records of the block, flattened: record j belongs to the tile i
+  // staged records of the range, flattened: record j belongs to the tile i
   // with pre_staged[i] <= j < pre_staged[i + 1]
-  const uint32_t tiles = (uint32_t)std::min<uint64_t>(kBlockTiles, a.n_tiles - blk * kBlockTiles);
   for (uint32_t j0 = 0; j0 < staged_total; j0 += kThreads * kPlaceBatch) {
     uint32_t v[kPlaceBatch];
     uint64_t dst[kPlaceBatch];
@@ -778,7 +836,7 @@ __device__ void encode_place(const EncArgs& a) {
           else hi = mid;
         }
         const uint32_t r = j - sh.pre_staged[lo];
-        v[u] = a.stage[(blk * kBlockTiles + lo) * kStageSlot + r];
+        v[u] = a.stage[(t0 + lo) * kStageSlot + r];
         dst[u] = base + sh.pre_all[lo] + r;
       }
     }
@@ -786,26 +844,39 @@ __device__ void encode_place(const EncArgs& a) {
     for (uint32_t u = 0; u < kPlaceBatch; ++u)
       if (dst[u] != ~0ull) put_record<kVariant>(a, dst[u], v[u] & 0xFFFF, v[u] >> 16);
   }
-  if (!sh.overflow) return;  // uniform
+  if (!any_over) return;  // uniform
 
-  // tiles whose escapes overflowed their slot: read them again
+  // tiles whose escapes overflowed their slot: encoded again, records in
+  // element order through LDS windows to word stores.  The thread index is
+  // passed through an empty asm statement in each iteration, so the compiler
+  // cannot hoist the per-thread address arithmetic of the loop body out of
+  // the loop (holding it live across iterations costs the kernel about 40
+  // registers, which the common path pays in occupancy).
   uint64_t table_cb = ~0ull;
   for (uint32_t i = 0; i < tiles; ++i) {
     const uint32_t n_i = sh.pre_all[i + 1] - sh.pre_all[i];
     if (n_i <= kStageSlot) continue;  // uniform
-    const uint64_t tt = blk * kBlockTiles + i;
+    uint32_t tid_i = tid;
+    asm volatile("" : "+v"(tid_i));
+    const uint64_t tt = t0 + i;
     const uint64_t cbi = a.seg_chunks ? codebook_of_chunk(tt >> (kBf16 ? 3 : 2), a.seg_chunks) : 0;
+    const TileIn in = kBf16 ? load_tile_bf16(a, tt, tid_i) : load_tile_e5m2(a, tt, tid_i);
     if (cbi != table_cb) {
-      build_table<kVariant>(a, esh, cbi, kBf16 ? 256u : 32u);
+      build_table<kVariant>(a, esh, cbi, kBf16 ? 256u : 32u, tid_i);
       table_cb = cbi;
     }
-    const TileIn in = kBf16 ? load_tile_bf16(a, tt) : load_tile_e5m2(a, tt);
-    const TileEsc r = kBf16 ? encode_tile_bf16<kVariant>(a, esh, tt, in, false) : encode_tile_e5m2(a, esh, tt, in, false);
-    const uint64_t at = base + sh.pre_all[i];
-    auto direct = [&](uint32_t k, uint32_t pos, uint32_t val) { put_record<kVariant>(a, at + k, pos, val); };
-    if (kBf16) for_each_escape_bf16(a, tt, r, direct);
-    else for_each_escape_e5m2(a, tt, r, direct);
-    __syncthreads();  // esh is reused by the next tile
+    const TileEsc r = kBf16 ? encode_tile_bf16<kVariant>(a, esh, tt, in, false, tid_i)
+                            : encode_tile_e5m2(a, esh, tt, in, false, tid_i);
+    for (uint32_t w0 = 0; w0 < n_i; w0 += kPlaceRecs) {  // BF16: one window per 2048 records
+      auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) {
+        if (k - w0 < kPlaceRecs) sh.rec[k - w0] = pos | (val << 16);
+      };
+      if (kBf16) for_each_escape_bf16<true>(a, tt, r, stage, w0, kPlaceRecs, tid_i, &in);
+      else for_each_escape_e5m2<true>(a, tt, r, stage, w0, kPlaceRecs, tid_i, &in);
+      __syncthreads();
+      write_records<kVariant>(a, sh.rec, base + sh.pre_all[i] + w0, std::min<uint32_t>(kPlaceRecs, n_i - w0), tid_i);
+      __syncthreads();  // sh.rec and esh are reused
+    }
   }
 }
 
@@ -887,15 +958,77 @@ __device__ uint64_t wave_lower_bound(const uint8_t* esc, uint64_t lo, uint64_t h
   return lo + (uint64_t)__builtin_ctzll(__ballot(hit));
 }
 
+// Four records of the escape section: records 4q .. 4q+3 fill its words
+// 3q .. 3q+2 exactly (the section is 256-aligned), and bytes 1 and 2 of word
+// 3q-1 hold the position of record 4q-1.  One group is read with word
+// loads and unpacked with fixed shifts, the inverse of the encoder's packing.
+struct RecGroup {
+  uint32_t pos[4], val[4];
+  uint32_t prev_pos;  // position of record 4q-1 (0 for q == 0)
+};
+
+__device__ inline RecGroup load_rec_group(const DecArgs& a, uint64_t esc, uint64_t q) {
+  const uint64_t b = esc + 12 * q;
+  uint32_t w0 = 0, w1, w2, w3;
+  if (b + 12 <= a.in_bytes) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(a.in + b);
+    if (q > 0) w0 = p[-1];
+    w1 = p[0];
+    w2 = p[1];
+    w3 = p[2];
+  } else {  // the stream's last bytes: nothing past in_bytes is read
+    uint32_t w[3] = {0, 0, 0};
+    for (uint32_t i = 0; i < 12 && b + i < a.in_bytes; ++i) w[i >> 2] |= (uint32_t)a.in[b + i] << (8 * (i & 3));
+    if (q > 0) w0 = *reinterpret_cast<const uint32_t*>(a.in + b - 4);
+    w1 = w[0];
+    w2 = w[1];
+    w3 = w[2];
+  }
+  RecGroup g;
+  g.pos[0] = w1 & 0xFFFFu;
+  g.val[0] = (w1 >> 16) & 0xFFu;
+  g.pos[1] = (w1 >> 24) | ((w2 & 0xFFu) << 8);
+  g.val[1] = (w2 >> 8) & 0xFFu;
+  g.pos[2] = w2 >> 16;
+  g.val[2] = w3 & 0xFFu;
+  g.pos[3] = (w3 >> 8) & 0xFFFFu;
+  g.val[3] = w3 >> 24;
+  g.prev_pos = (w0 >> 8) & 0xFFFFu;
+  return g;
+}
+
+constexpr uint32_t kScanGroups = 1;  // record groups per thread and step of a long chunk (more cost occupancy)
+
+// The tile's chunk's record range and, for a short chunk (at most kThreads
+// record groups), this thread's group: read before the tile's dense loads
+// are issued, so that waiting for the records does not mean waiting for the
+// dense data queued behind them (loads complete in issue order).
+struct EscFetch {
+  uint64_t lo, hi;  // the chunk's records (offsets table)
+  RecGroup G;       // group lo / 4 + thread index, short chunk only
+};
+
+template <uint32_t kDecTile>
+__device__ inline EscFetch fetch_escapes(const DecArgs& a, const Header& h, uint64_t tile) {
+  EscFetch f;
+  const uint64_t chunk = tile / (kChunk / kDecTile);
+  const uint8_t* offs = a.in + h.s.offsets;
+  f.lo = ld64(offs + 8 * chunk);
+  f.hi = ld64(offs + 8 * (chunk + 1));
+  const uint64_t g_lo = f.lo / 4, g_hi = (f.hi + 3) / 4;
+  const uint64_t g = g_lo + threadIdx.x;
+  // an inconsistent range is rejected by stage_escapes; nothing is read for it
+  if (f.lo <= f.hi && f.hi <= h.e && g_hi - g_lo <= kThreads && g < g_hi) f.G = load_rec_group(a, h.s.esc, g);
+  return f;
+}
+
 // Stage this tile's escapes in LDS: a bitmap over the tile's elements and
 // the raw exponents.  Every record of the chunk is checked by exactly one of
 // the chunk's tiles (in window, strictly increasing, valid value).  Returns
 // false (the same in every thread) if the stream is invalid.
-constexpr uint32_t kScanRecs = 4;  // records per thread of a chunk staged without a search
-
 template <uint32_t kDecTile>
-__device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, uint32_t* bitmap, uint8_t* vals,
-                              uint32_t* s_range, int* s_err) {
+__device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, const EscFetch& f, uint32_t* bitmap,
+                              uint8_t* vals, uint32_t* s_range, int* s_err) {
   const uint32_t tid = threadIdx.x;
   const uint64_t chunk = tile / (kChunk / kDecTile);
   const uint32_t q = (uint32_t)(tile % (kChunk / kDecTile));
@@ -903,47 +1036,51 @@ __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, 
   const uint32_t win_lo = q * (uint32_t)kDecTile;
   const uint32_t win_len = (uint32_t)std::min<uint64_t>(kDecTile, chunk_len - win_lo);
   const bool last_in_chunk = win_lo + win_len == chunk_len;
-  const uint8_t* offs = a.in + h.s.offsets;
-  const uint64_t lo = ld64(offs + 8 * chunk), hi = ld64(offs + 8 * (chunk + 1));
+  const uint64_t lo = f.lo, hi = f.hi;
   bool ok = lo <= hi && hi <= h.e;
   if (chunk == 0 && lo != 0) ok = false;
   if (chunk == h.chunks - 1 && hi != h.e) ok = false;
   if (!ok) return false;  // uniform: every thread read the same words
   const uint32_t vmax = a.dtype == SPLITZIP_BF16 ? 256u : 32u;
 
-  if (hi - lo <= (uint64_t)kScanRecs * kThreads) {  // uniform
-    // short chunk: every tile of the chunk loads all of its records at once
-    // (no search, whose dependent loads would lengthen the tile's critical
-    // path), checks all of them and stages those in its window
-    uint32_t pos[kScanRecs], prev1[kScanRecs], val[kScanRecs];
+  // records [ra, rb) of group g: each must lie in [p_lo, p_lo + p_len) and
+  // follow its predecessor in the range; in-window ones are staged
+  auto check_group = [&](uint64_t g, uint64_t ra, uint64_t rb, uint32_t p_lo, uint32_t p_len, const RecGroup& G,
+                         bool& bad) {
+    const uint64_t r0 = 4 * g;  // record j of the group is r0 + j
+    const uint32_t j_lo = ra > r0 ? (uint32_t)(ra - r0) : 0u;  // < 4 for a group that meets the range
+    const uint32_t j_hi = (uint32_t)std::min<uint64_t>(4, rb - r0);
+    const bool first = ra >= r0;  // the range's first record is in this group (at j_lo)
 #pragma unroll
-    for (uint32_t k = 0; k < kScanRecs; ++k) {
-      const uint64_t r = lo + tid + k * kThreads;
-      pos[k] = ~0u;  // no record
-      if (r < hi) {
-        const uint8_t* rec = a.in + h.s.esc + 3 * r;
-        pos[k] = record_pos(rec);
-        val[k] = rec[2];
-        prev1[k] = r > lo ? record_pos(rec - 3) + 1 : 0;  // predecessor's position + 1, 0 for the first
+    for (uint32_t j = 0; j < 4; ++j) {
+      if (j < j_lo || j >= j_hi) continue;
+      const uint32_t pos = G.pos[j], val = G.val[j];
+      const uint32_t prev1 = (first && j == j_lo) ? 0u : (j == 0 ? G.prev_pos : G.pos[j > 0 ? j - 1 : 0]) + 1;
+      if (pos - p_lo >= p_len || val >= vmax || prev1 > pos) {  // pos - p_lo wraps for pos < p_lo
+        bad = true;
+        continue;
+      }
+      const uint32_t local = pos - win_lo;  // wraps for pos < win_lo
+      if (local < win_len) {
+        vals[local] = (uint8_t)val;
+        atomicOr(&bitmap[local >> 5], 1u << (local & 31));
       }
     }
+  };
+
+  const uint64_t g_lo = lo / 4, g_hi = (hi + 3) / 4;  // record groups of the chunk
+  if (g_hi - g_lo <= kThreads) {  // uniform
+    // short chunk (up to 1024 records): every tile of the chunk has loaded
+    // all of its records, a group per thread (no search, whose dependent
+    // loads would lengthen the tile's critical path); it checks all of them
+    // and stages those in its window
+    const uint64_t g = g_lo + tid;
+    const RecGroup& G = f.G;
     for (uint32_t i = tid; i < kDecTile / 32; i += kThreads) bitmap[i] = 0;
     if (tid == 0) *s_err = 0;
     __syncthreads();
     bool bad = false;
-#pragma unroll
-    for (uint32_t k = 0; k < kScanRecs; ++k) {
-      if (pos[k] == ~0u) continue;
-      if (pos[k] >= chunk_len || val[k] >= vmax || prev1[k] > pos[k]) {
-        bad = true;
-        continue;
-      }
-      const uint32_t local = pos[k] - win_lo;  // wraps for pos < win_lo
-      if (local < win_len) {
-        vals[local] = (uint8_t)val[k];
-        atomicOr(&bitmap[local >> 5], 1u << (local & 31));
-      }
-    }
+    if (g < g_hi) check_group(g, lo, hi, 0, (uint32_t)chunk_len, G, bad);
     if (bad) *s_err = 1;
     __syncthreads();
     return *s_err == 0;
@@ -962,30 +1099,18 @@ __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, 
   __syncthreads();
   const uint64_t ra = lo + s_range[0], rb = lo + s_range[1];
   bool bad = false;
-  // kScanRecs records per thread per step, their loads issued together
-  for (uint64_t r0 = ra; r0 < rb; r0 += (uint64_t)kScanRecs * kThreads) {
-    uint32_t pos[kScanRecs], prev1[kScanRecs], val[kScanRecs];
+  // the tile's records, a group per thread per step
+  for (uint64_t g0 = ra / 4; g0 < (rb + 3) / 4; g0 += (uint64_t)kScanGroups * kThreads) {
+    RecGroup G[kScanGroups];
 #pragma unroll
-    for (uint32_t k = 0; k < kScanRecs; ++k) {
-      const uint64_t r = r0 + k * kThreads + tid;
-      pos[k] = ~0u;  // no record
-      if (r < rb) {
-        const uint8_t* rec = a.in + h.s.esc + 3 * r;
-        pos[k] = record_pos(rec);
-        val[k] = rec[2];
-        prev1[k] = r > ra ? record_pos(rec - 3) + 1 : 0;  // predecessor's position + 1, 0 for the first
-      }
+    for (uint32_t k = 0; k < kScanGroups; ++k) {
+      const uint64_t g = g0 + k * kThreads + tid;
+      if (g < (rb + 3) / 4) G[k] = load_rec_group(a, h.s.esc, g);
     }
 #pragma unroll
-    for (uint32_t k = 0; k < kScanRecs; ++k) {
-      if (pos[k] == ~0u) continue;
-      const uint32_t local = pos[k] - win_lo;  // wraps for pos < win_lo
-      if (pos[k] < win_lo || local >= win_len || val[k] >= vmax || prev1[k] > pos[k]) {
-        bad = true;
-        continue;
-      }
-      vals[local] = (uint8_t)val[k];
-      atomicOr(&bitmap[local >> 5], 1u << (local & 31));
+    for (uint32_t k = 0; k < kScanGroups; ++k) {
+      const uint64_t g = g0 + k * kThreads + tid;
+      if (g < (rb + 3) / 4) check_group(g, ra, rb, win_lo, win_len, G[k], bad);
     }
   }
   if (bad) *s_err = 1;
@@ -1050,7 +1175,8 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
   const bool fast = first + kDecTile <= a.n;  // same in every thread
   const uint8_t* nib_t = a.in + h.s.nib + first / 2;
   const uint8_t* sm_t = a.in + h.s.sm + first;
-  // issue the tile's dense loads first: the escape staging overlaps them
+  const EscFetch fe = fetch_escapes<kDecTile>(a, h, tile);
+  // then the tile's dense loads: the escape staging overlaps them
   uint32_t nibs[kGroups];
   uint2 sms[kGroups];
   if (fast) {
@@ -1066,7 +1192,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
     const uint32_t pair = lut4((c & 0xFu) | ((c >> 4) << 8), l0, l1, l2, l3);  // bytes 0, 1: the two exponents
     tab2[c] = ((pair & 0xFFu) << 7) | (((pair >> 8) & 0xFFu) << 23);
   }
-  if (!stage_escapes<kDecTile>(a, h, tile, bitmap, vals, s_range, &s_err)) {  // its barriers publish tab2
+  if (!stage_escapes<kDecTile>(a, h, tile, fe, bitmap, vals, s_range, &s_err)) {  // its barriers publish tab2
     if (threadIdx.x == 0) report_corrupt(a.status);
     return;
   }
@@ -1175,7 +1301,8 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
   const bool fast = first + kDecTile <= a.n;  // same in every thread
   const uint8_t* nib_t = a.in + h.s.nib + first / 2;
   const uint8_t* sm_t = a.in + h.s.sm + 3 * (first / 8);
-  // issue the tile's dense loads first: the escape staging overlaps them
+  const EscFetch fe = fetch_escapes<kDecTile>(a, h, tile);
+  // then the tile's dense loads: the escape staging overlaps them
   uint2 pn[kGroups];
   uint32_t p0[kGroups], p1[kGroups];
   if (fast) {
@@ -1197,7 +1324,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
     const uint32_t pair = lut4((c & 0xFu) | ((c >> 4) << 8), l0, l1, l2, l3);  // bytes 0, 1: the two exponents
     tab2[c] = (uint16_t)((pair & 0xFFu) << 2 | ((pair >> 8) & 0xFFu) << 10);
   }
-  if (!stage_escapes<kDecTile>(a, h, tile, bitmap, vals, s_range, &s_err)) {  // its barriers publish tab2
+  if (!stage_escapes<kDecTile>(a, h, tile, fe, bitmap, vals, s_range, &s_err)) {  // its barriers publish tab2
     if (threadIdx.x == 0) report_corrupt(a.status);
     return;
   }
@@ -1282,6 +1409,7 @@ __global__ __launch_bounds__(kThreads) void decode_top8_kernel(DecArgs a) {
   const bool fast = first + kDecTile <= a.n;  // same in every thread
   const uint8_t* code_t = a.in + h.s.nib + 3 * (first / 8);
   const uint8_t* sm_t = a.in + h.s.sm + first;
+  const EscFetch fe = fetch_escapes<kDecTile>(a, h, tile);
   // the 3 code bytes of a thread lie in two aligned dwords; the last
   // thread's second dword reaches 4 bytes past the tile's codes, still
   // inside the stream (the sign|mantissa section follows)
@@ -1297,7 +1425,7 @@ __global__ __launch_bounds__(kThreads) void decode_top8_kernel(DecArgs a) {
     }
   }
   const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4);
-  if (!stage_escapes<kDecTile>(a, h, tile, bitmap, vals, s_range, &s_err)) {
+  if (!stage_escapes<kDecTile>(a, h, tile, fe, bitmap, vals, s_range, &s_err)) {
     if (threadIdx.x == 0) report_corrupt(a.status);
     return;
   }
@@ -1603,10 +1731,15 @@ int compress_impl(int dtype, int variant, const void* d_in, size_t n_elems, cons
   if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
   encode_sums_kernel<<<(uint32_t)divup(blocks, kThreads), kThreads, 0, stream>>>(e);
   if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
-  if (dtype == SPLITZIP_FP8_E5M2) encode_place_e5m2_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(e);
-  else if (variant == kSentinel) encode_place_sentinel_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(e);
-  else if (variant == kTop8) encode_place_top8_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(e);
-  else encode_place_bf16_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(e);
+  // tiles per encode_place workgroup: the power of two from 8 to 64 that
+  // gives about kPlaceWgs workgroups
+  e.place_tiles = 8;
+  while (e.place_tiles < kBlockTiles && (uint64_t)e.place_tiles * kPlaceWgs < n_tiles) e.place_tiles *= 2;
+  const uint32_t place_wgs = (uint32_t)divup(n_tiles, e.place_tiles);
+  if (dtype == SPLITZIP_FP8_E5M2) encode_place_e5m2_kernel<<<place_wgs, kThreads, 0, stream>>>(e);
+  else if (variant == kSentinel) encode_place_sentinel_kernel<<<place_wgs, kThreads, 0, stream>>>(e);
+  else if (variant == kTop8) encode_place_top8_kernel<<<place_wgs, kThreads, 0, stream>>>(e);
+  else encode_place_bf16_kernel<<<place_wgs, kThreads, 0, stream>>>(e);
   if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
   return SPLITZIP_OK;
 }
