@@ -84,7 +84,9 @@ int splitzip_calibrate(int dtype, const void* host_samples, size_t n_elems, uint
  * 8192-element tile 2052 bytes (a count and a staging slot for up to 512
  * escape records), per 64 tiles 8 bytes and per 4096 tiles 8 bytes, with
  * 256-byte alignment.  Returns 0 for an invalid dtype,
- * n_codebooks == 0 or n_elems > 2^40. */
+ * n_codebooks == 0 or n_elems > 2^36 (the largest n any call accepts: every
+ * kernel grid then stays below 2^32 work-items; 2^36 BF16 elements are
+ * 128 GiB). */
 size_t splitzip_max_compressed_size(int dtype, size_t n_elems, uint32_t n_codebooks);
 
 /* Encode (technical summary, "Estrategia de Codificacion"; abstract; English

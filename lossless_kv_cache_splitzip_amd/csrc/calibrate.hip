@@ -111,7 +111,7 @@ int splitzip_calibrate_device(int dtype, const void* d_samples, size_t n_elems, 
                               uint32_t n_codebooks, uint8_t* d_codebooks_out, void* d_work, size_t work_bytes,
                               hipStream_t stream) {
   const size_t need = splitzip_calibrate_device_work_bytes(dtype, n_codebooks);
-  if (need == 0 || n_elems > (1ull << 40) || (d_samples == nullptr && n_elems > 0) || d_codebooks_out == nullptr ||
+  if (need == 0 || n_elems > (1ull << 36) || (d_samples == nullptr && n_elems > 0) || d_codebooks_out == nullptr ||
       d_work == nullptr || (reinterpret_cast<uintptr_t>(d_samples) & 15) != 0 ||
       (reinterpret_cast<uintptr_t>(d_work) & 7) != 0)
     return SPLITZIP_E_INVALID;

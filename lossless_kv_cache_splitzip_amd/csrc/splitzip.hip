@@ -50,7 +50,7 @@ constexpr uint32_t kDecTileBf16 = 8192;   // elements per decode workgroup (meas
 constexpr uint32_t kDecTileE5m2 = 16384;  // E5M2 16384; larger tiles cost occupancy, smaller ones overhead)
 constexpr uint32_t kMagic = 0x00315A53u;
 constexpr uint32_t kMaxK = 65535;
-constexpr uint64_t kMaxN = 1ull << 40;
+constexpr uint64_t kMaxN = 1ull << 36;  // every grid then stays below 2^32 work-items
 constexpr int kCbPerPrep = 128;
 constexpr uint8_t kEsc = 0x10;  // table entry of an exponent outside the codebook
 

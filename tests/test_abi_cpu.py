@@ -55,7 +55,8 @@ def test_max_compressed_size():
             assert cap % 8 == 0
     assert sz.splitzip_max_compressed_size(3, 10, 1) == 0
     assert sz.splitzip_max_compressed_size(O.BF16, 10, 0) == 0
-    assert sz.splitzip_max_compressed_size(O.BF16, (1 << 40) + 1, 1) == 0
+    assert sz.splitzip_max_compressed_size(O.BF16, (1 << 36) + 1, 1) == 0
+    assert sz.splitzip_max_compressed_size(O.BF16, 1 << 36, 1) > 0
 
 
 def test_argument_errors_return_before_any_gpu_work():
