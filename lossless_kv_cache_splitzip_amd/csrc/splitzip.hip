@@ -11,7 +11,9 @@
 // is stated in include/splitzip.h.
 //
 // GPU design (ours):
-//   prep          header, codebooks and the zero padding between sections.
+//   prep          header, codebooks and the zero padding between sections:
+//                 one extra workgroup of a later launch when the codebooks
+//                 fit the kernel arguments, else launches of their own.
 //   encode_dense  one workgroup per tile (8192 BF16 or 16384 E5M2 elements):
 //                 16-byte loads issued before the codebook tables are built
 //                 in LDS, then codes, nibbles and sign|mantissa bytes with
@@ -208,13 +210,15 @@ __device__ inline void put_le(uint8_t* p, uint64_t v, int bytes) {
   for (int i = 0; i < bytes; ++i) p[i] = (uint8_t)(v >> (8 * i));
 }
 
-// Header, codebooks and zero padding.
-__global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
-  const uint64_t gtid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-  const uint64_t gsize = (uint64_t)gridDim.x * kThreads;
+// Header, codebooks and zero padding, by workgroup wg of n_wg.  Header bytes
+// 16..31 (E and S) are written here only for n == 0; otherwise the placement
+// pass writes them, possibly in the same launch.
+__device__ void prep_work(const PrepArgs& a, uint32_t wg, uint32_t n_wg) {
+  const uint64_t gtid = (uint64_t)wg * kThreads + threadIdx.x;
+  const uint64_t gsize = (uint64_t)n_wg * kThreads;
   for (uint64_t i = gtid; i < (uint64_t)a.cb_count * 16; i += gsize)
     a.out[64 + 16 * (uint64_t)a.cb_first + i] = a.cbs[i];
-  if (!a.main || blockIdx.x != 0) return;
+  if (!a.main || wg != 0) return;
   const uint32_t t = threadIdx.x;
   // zero padding after the offsets, the nibbles and the sign|mantissa bytes
   const uint64_t ends[3] = {a.offsets + 8 * (a.chunks + 1), a.nib + a.code_bytes, a.sm + a.sm_bytes};
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     else if (t == 6) { v = a.dtype; }
     else if (t == 7) { v = 16; }
     else if (t < 16) { v = a.n; off = t - 8; }
-    else if (t < 32) { v = (a.n == 0 && t >= 24) ? a.esc : 0; off = t & 7; }
+    else if (t < 32) { if (a.n != 0) return; v = t >= 24 ? a.esc : 0; off = t & 7; }
     else if (t < 36) { v = a.chunks; off = t - 32; }
     else if (t < 40) { v = a.k; off = t - 36; }
     else if (t < 48) { v = a.seg_stored; off = t - 40; }
@@ -243,10 +247,12 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) { prep_work(a, blockIdx.x, gridDim.x); }
+
 // ---------------------------------------------------------- encode kernels
 //
-// Three launches after prep_kernel; no workgroup waits on another, so no
-// launch needs co-residency:
+// Three launches (two with at most 64 blocks: no encode_sums); no workgroup
+// waits on another, so no launch needs co-residency:
 //   encode_dense  one workgroup per 8192-element tile: dense encode (codes,
 //                 sign|mantissa) and element-order escape ranks.  The tile's
 //                 escape count goes to the workspace; when it holds at most
@@ -271,6 +277,10 @@ struct EncArgs {
   uint64_t* super_sum;    // per 64 blocks: escapes in them
   uint64_t* out_bytes;
   uint32_t place_tiles;   // tiles per encode_place workgroup: 8, 16, 32 or 64
+  uint32_t cb_args;       // codebooks read from prep.cbs (all of them fit), else from the stream
+  uint32_t prep_in;       // header, codebooks and padding written by: 0 prep_kernel, 1 encode_sums, 2 encode_place
+  uint32_t sums_in_place; // at most 64 blocks: encode_place sums the lower tiles itself, encode_sums is not launched
+  PrepArgs prep;          // the header work folded into a later launch (prep_in 1 or 2)
 };
 
 constexpr uint32_t kStageSlot = 512;  // staged escape records per tile
@@ -329,7 +339,7 @@ __device__ inline void build_table(const EncArgs& a, EncShared& sh, uint64_t cbi
   constexpr uint8_t kEscEntry = kVariant == kSentinel ? (kEsc | 15) : kEsc;
   if (tid < entries) sh.table[tid] = kEscEntry;
   __syncthreads();
-  if (tid < kCodes) sh.table[a.out[64 + 16 * cbi + tid]] = (uint8_t)tid;
+  if (tid < kCodes) sh.table[a.cb_args ? a.prep.cbs[16 * cbi + tid] : a.out[64 + 16 * cbi + tid]] = (uint8_t)tid;
   __syncthreads();
   if (entries == 32) {  // E5M2 per-position words, from the exponent table
     const uint32_t b = tid & 0xFFu;
@@ -697,6 +707,10 @@ __global__ __launch_bounds__(kThreads) void encode_dense_top8_kernel(EncArgs a) 
 // One thread per block of 64 tiles, one wave per 64 blocks (a super-block):
 // block sums, and each wave's total as its super-block sum.
 __global__ __launch_bounds__(kThreads) void encode_sums_kernel(EncArgs a) {
+  if (a.prep_in == 1 && blockIdx.x == gridDim.x - 1) {  // the launch's extra workgroup
+    prep_work(a.prep, 0, 1);
+    return;
+  }
   const uint64_t blk = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
   const uint64_t t0 = blk * kBlockTiles, t1 = std::min<uint64_t>(t0 + kBlockTiles, a.n_tiles);
   uint64_t sum = 0;
@@ -766,6 +780,10 @@ __device__ void encode_place(const EncArgs& a) {
   constexpr uint64_t kRec = kVariant == kSentinel ? 1 : 3;  // stream bytes per escape
   __shared__ PlaceShared sh;
   __shared__ EncShared esh;
+  if (a.prep_in == 2 && blockIdx.x == gridDim.x - 1) {  // the launch's extra workgroup
+    prep_work(a.prep, 0, 1);
+    return;
+  }
   const uint32_t tid = threadIdx.x;
   const uint64_t t0 = (uint64_t)blockIdx.x * a.place_tiles;
   const uint32_t tiles = (uint32_t)std::min<uint64_t>(a.place_tiles, a.n_tiles - t0);
@@ -777,11 +795,16 @@ __device__ void encode_place(const EncArgs& a) {
   const bool over = cnt > kStageSlot;
 
   // base: the first wave adds the lower blocks of the super-block, the
-  // second the lower tiles of the block, all waves the lower super-blocks
+  // second the lower tiles of the block, all waves the lower super-blocks;
+  // with at most 64 blocks (no block sums) all waves add the lower tiles
   uint64_t lower = 0;
-  for (uint64_t i = tid; i < (blk >> 6); i += kThreads) lower += a.super_sum[i];
-  if (tid < (blk & 63)) lower += a.block_sum[(blk & ~63ull) + tid];
-  if (tid >= 64 && tid - 64 < below) lower += a.tile_count[blk * kBlockTiles + (tid - 64)];
+  if (a.sums_in_place) {
+    for (uint32_t i = tid; i < (uint32_t)t0; i += kThreads) lower += a.tile_count[i];
+  } else {
+    for (uint64_t i = tid; i < (blk >> 6); i += kThreads) lower += a.super_sum[i];
+    if (tid < (blk & 63)) lower += a.block_sum[(blk & ~63ull) + tid];
+    if (tid >= 64 && tid - 64 < below) lower += a.tile_count[blk * kBlockTiles + (tid - 64)];
+  }
   {
     // wave sum of u64 through two u32 halves; one lane per wave stores it
     uint64_t v = lower;
@@ -1678,8 +1701,10 @@ int compress_impl(int dtype, int variant, const void* d_in, size_t n_elems, cons
   uint8_t* out = static_cast<uint8_t*>(d_out);
   const Workspace w = workspace_of(out, dtype, n, n_codebooks, variant);
 
-  for (uint32_t first = 0; first < n_codebooks; first += kCbPerPrep) {
-    PrepArgs p;
+  // header, codebooks and padding: a launch of their own when the stream is
+  // empty or the codebooks do not fit the kernel arguments; otherwise folded
+  // into a later launch as one extra workgroup
+  auto prep_args = [&](PrepArgs& p, uint32_t first) {
     memset(&p, 0, sizeof(p));
     p.out = out;
     p.n = n;
@@ -1699,9 +1724,16 @@ int compress_impl(int dtype, int variant, const void* d_in, size_t n_elems, cons
     p.cb_count = std::min<uint32_t>(kCbPerPrep, n_codebooks - first);
     p.main = first == 0;
     memcpy(p.cbs, h_codebooks + 16ull * first, 16ull * p.cb_count);
-    const uint32_t blocks = (uint32_t)std::max<uint64_t>(1, divup(16ull * p.cb_count, kThreads));
-    prep_kernel<<<blocks, kThreads, 0, stream>>>(p);
-    if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
+  };
+  const bool cb_args = n > 0 && n_codebooks <= (uint32_t)kCbPerPrep;
+  if (!cb_args) {
+    for (uint32_t first = 0; first < n_codebooks; first += kCbPerPrep) {
+      PrepArgs p;
+      prep_args(p, first);
+      const uint32_t blocks = (uint32_t)std::max<uint64_t>(1, divup(16ull * p.cb_count, kThreads));
+      prep_kernel<<<blocks, kThreads, 0, stream>>>(p);
+      if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
+    }
   }
   if (n == 0) return SPLITZIP_OK;
 
@@ -1721,21 +1753,28 @@ int compress_impl(int dtype, int variant, const void* d_in, size_t n_elems, cons
   e.block_sum = w.block_sum;
   e.super_sum = w.super_sum;
   e.out_bytes = d_out_bytes;
-  const uint32_t tiles = (uint32_t)n_tiles;  // n <= 2^40 -> at most 2^27 tiles
+  const uint32_t tiles = (uint32_t)n_tiles;  // n <= 2^36 -> at most 2^23 tiles
   const uint64_t blocks = divup(n_tiles, kBlockTiles);
   e.n_blocks = blocks;
+  // tiles per encode_place workgroup: the power of two from 8 to 64 that
+  // gives about kPlaceWgs workgroups
+  e.place_tiles = 8;
+  while (e.place_tiles < kBlockTiles && (uint64_t)e.place_tiles * kPlaceWgs < n_tiles) e.place_tiles *= 2;
+  e.cb_args = cb_args;
+  e.sums_in_place = blocks <= 64;
+  e.prep_in = cb_args ? (e.sums_in_place ? 2 : 1) : 0;
+  if (cb_args) prep_args(e.prep, 0);
+  else memset(&e.prep, 0, sizeof(e.prep));
   if (dtype == SPLITZIP_FP8_E5M2) encode_dense_e5m2_kernel<<<tiles, kThreads, 0, stream>>>(e);
   else if (variant == kSentinel) encode_dense_sentinel_kernel<<<tiles, kThreads, 0, stream>>>(e);
   else if (variant == kTop8) encode_dense_top8_kernel<<<tiles, kThreads, 0, stream>>>(e);
   else encode_dense_bf16_kernel<<<tiles, kThreads, 0, stream>>>(e);
   if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
-  encode_sums_kernel<<<(uint32_t)divup(blocks, kThreads), kThreads, 0, stream>>>(e);
-  if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
-  // tiles per encode_place workgroup: the power of two from 8 to 64 that
-  // gives about kPlaceWgs workgroups
-  e.place_tiles = 8;
-  while (e.place_tiles < kBlockTiles && (uint64_t)e.place_tiles * kPlaceWgs < n_tiles) e.place_tiles *= 2;
-  const uint32_t place_wgs = (uint32_t)divup(n_tiles, e.place_tiles);
+  if (!e.sums_in_place) {
+    encode_sums_kernel<<<(uint32_t)divup(blocks, kThreads) + (e.prep_in == 1), kThreads, 0, stream>>>(e);
+    if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
+  }
+  const uint32_t place_wgs = (uint32_t)divup(n_tiles, e.place_tiles) + (e.prep_in == 2);
   if (dtype == SPLITZIP_FP8_E5M2) encode_place_e5m2_kernel<<<place_wgs, kThreads, 0, stream>>>(e);
   else if (variant == kSentinel) encode_place_sentinel_kernel<<<place_wgs, kThreads, 0, stream>>>(e);
   else if (variant == kTop8) encode_place_top8_kernel<<<place_wgs, kThreads, 0, stream>>>(e);
