@@ -1,12 +1,13 @@
-"""The decoder's acceptance test equals the oracle's: streams damaged at
-random in the chunk-offset table, the escape records and the E / S header
-fields, or handed over with fewer bytes than they hold, are rejected by the
-GPU (d_status = E_CORRUPT) exactly when the oracle's validation rejects them;
-a damaged stream that is still valid (an escape moved to another free
-position, an exponent replaced by another in range) decodes to the oracle's
-result bit for bit.  Short chunks (the decoder loads all of a chunk's records
-in every tile) and long chunks (it searches for the tile's records) are both
-covered, for BF16 and E5M2.
+"""The decoders' acceptance test equals the oracle's: streams damaged at
+random in the chunk-offset table, the codes, the escape section and the E / S
+header fields, or handed over with fewer bytes than they hold, are rejected by
+the GPU (d_status = E_CORRUPT) exactly when the oracle's validation rejects
+them; a damaged stream that is still valid (another code, an escape moved to
+another free position, an exponent replaced by another in range) decodes to
+the oracle's result bit for bit.  Short chunks (the decoder loads all of a
+chunk's records in every tile) and long chunks (it searches for the tile's
+records) are both covered, for BF16 and E5M2, and so are the two ablation
+variants' decoders.
 """
 import numpy as np
 import pytest
@@ -22,45 +23,74 @@ sz = pytest.importorskip("lossless_kv_cache_splitzip_amd")
 DEV = "cuda"
 
 
-def _gpu_status_and_output(stream: np.ndarray, n: int, dtype: int, in_bytes: int):
-    dev = torch.from_numpy(stream).to(DEV)
-    y, st = sz.decompress(dev, n, dtype, in_bytes=in_bytes)
-    torch.cuda.synchronize()
-    return int(st.item()), kvsynth.to_numpy_bits(y)
+def _a256(x):
+    return (x + 255) // 256 * 256
 
 
-def _mutations(good: np.ndarray, dtype: int, n: int, rng, count: int):
-    """(stream, in_bytes, label) cases, each damaged in one way."""
-    sec = O.sections(dtype, n, 1)
+def _layout(good: np.ndarray, n: int, code_bytes: int, rec: int):
+    """Offsets table, code section and escape section of a one-codebook stream."""
+    C = (n + 65535) // 65536
+    off0 = 64 + 16
+    code0 = _a256(off0 + 8 * (C + 1))
     E = u64(good, 16)
+    esc = u64(good, 24) - rec * E
+    return (off0, off0 + 8 * (C + 1)), (code0, code0 + code_bytes), esc, E
+
+
+def _mutations(good: np.ndarray, n: int, code_bytes: int, rec: int, rng, count: int):
+    """(stream, in_bytes, label) cases, each damaged in one way: a byte of the
+    offset table, of the codes or of the escape section; a record position
+    nudged by one or two records swapped (position records only); E or S in
+    the header off by a little; fewer bytes than the stream holds."""
+    (off0, off1), (code0, code1), esc, E = _layout(good, n, code_bytes, rec)
     S = good.size
-    off0, off1 = sec["offsets"], sec["offsets"] + 8 * (sec["chunks"] + 1)
-    esc = sec["esc"]
+    kinds = 7 if rec == 3 else 5
     for i in range(count):
         t = good.copy()
-        kind = i % 6
-        if kind == 0:  # a byte of the chunk-offset table
+        kind = i % kinds
+        if kind == 0:
             t[rng.integers(off0, off1)] = rng.integers(0, 256)
             yield t, S, "offset byte"
-        elif kind == 1 and E:  # a byte of an escape record
-            t[esc + rng.integers(0, 3 * E)] = rng.integers(0, 256)
-            yield t, S, "record byte"
-        elif kind == 2 and E:  # the low position byte of a record, nudged by one
-            r = int(rng.integers(0, E))
-            t[esc + 3 * r] = (int(t[esc + 3 * r]) + int(rng.choice([-1, 1]))) & 0xFF
-            yield t, S, "position nudge"
-        elif kind == 3 and E > 1:  # two neighbouring records swapped
-            r = int(rng.integers(0, E - 1))
-            a, b = esc + 3 * r, esc + 3 * r + 3
-            t[a:a + 3], t[b:b + 3] = good[b:b + 3], good[a:a + 3]
-            yield t, S, "records swapped"
-        elif kind == 4:  # E or S in the header off by a little
+        elif kind == 1:
+            t[rng.integers(code0, code1)] = rng.integers(0, 256)
+            yield t, S, "code byte"
+        elif kind == 2 and E:
+            t[esc + rng.integers(0, rec * E)] = rng.integers(0, 256)
+            yield t, S, "escape byte"
+        elif kind == 3:
             field = 16 if rng.integers(0, 2) else 24
             v = u64(good, field) + int(rng.choice([-3, -1, 1, 3]))
             t[field:field + 8] = np.frombuffer(np.uint64(v).tobytes(), np.uint8)
             yield t, S, "header E/S"
-        else:  # fewer bytes than the stream holds
+        elif kind == 4:
             yield t, S - int(rng.integers(1, 16)), "truncated"
+        elif kind == 5 and E:
+            r = int(rng.integers(0, E))
+            t[esc + 3 * r] = (int(t[esc + 3 * r]) + int(rng.choice([-1, 1]))) & 0xFF
+            yield t, S, "position nudge"
+        elif kind == 6 and E > 1:
+            r = int(rng.integers(0, E - 1))
+            a, b = esc + 3 * r, esc + 3 * r + 3
+            t[a:a + 3], t[b:b + 3] = good[b:b + 3], good[a:a + 3]
+            yield t, S, "records swapped"
+
+
+def _check(cases, gpu_decode, oracle_status, oracle_decode):
+    rejected = accepted = 0
+    for t, in_bytes, label in cases:
+        want = oracle_status(t[:in_bytes])
+        dev = torch.from_numpy(t).to(DEV)
+        y, st = gpu_decode(dev, in_bytes)
+        torch.cuda.synchronize()
+        got = int(st.item())
+        assert got == want, f"{label}: GPU status {got}, oracle {want}"
+        if want == O.OK:
+            accepted += 1
+            assert np.array_equal(kvsynth.to_numpy_bits(y), oracle_decode(t[:in_bytes])), f"{label}: output differs"
+        else:
+            rejected += 1
+    print(f"  rejected {rejected}, still valid {accepted}", flush=True)
+    assert rejected > 0 and accepted > 0
 
 
 CASES = [
@@ -72,11 +102,15 @@ CASES = [
 ]
 
 
+def _data(dtype, n, sigma, calib):
+    xh = kvsynth.to_numpy_bits(kvsynth.random_bits(n, dtype, seed=int(n) % 1000, sigma=sigma))
+    return xh, O.calibrate(dtype, xh[:calib])
+
+
 @pytest.mark.parametrize("dtype,n,sigma,calib", CASES,
                          ids=["bf16-short", "bf16-long", "e5m2-short", "e5m2-long"])
 def test_gpu_rejects_exactly_what_the_oracle_rejects(dtype, n, sigma, calib):
-    xh = kvsynth.to_numpy_bits(kvsynth.random_bits(n, dtype, seed=int(n) % 1000, sigma=sigma))
-    cb = O.calibrate(dtype, xh[:calib])
+    xh, cb = _data(dtype, n, sigma, calib)
     good = O.compress(dtype, xh, cb)
     E = u64(good, 16)
     per_chunk = E / max(1, (n + 65535) // 65536)
@@ -85,16 +119,23 @@ def test_gpu_rejects_exactly_what_the_oracle_rejects(dtype, n, sigma, calib):
         assert per_chunk > 1024  # the decoder's long-chunk path
     else:
         assert 0 < per_chunk <= 1024
-    rng = np.random.default_rng(n)
-    rejected = accepted = 0
-    for t, in_bytes, label in _mutations(good, dtype, n, rng, 120):
-        want = O.validate(t[:in_bytes], dtype, n)
-        got, y = _gpu_status_and_output(t, n, dtype, in_bytes)
-        assert got == want, f"{label}: GPU status {got}, oracle {want}"
-        if want == O.OK:
-            accepted += 1
-            assert np.array_equal(y, O.decompress(t[:in_bytes], dtype, n)), f"{label}: output differs"
-        else:
-            rejected += 1
-    print(f"  rejected {rejected}, still valid {accepted}", flush=True)
-    assert rejected > 0
+    code_bytes = (n + 1) // 2
+    _check(_mutations(good, n, code_bytes, 3, np.random.default_rng(n), 140),
+           lambda dev, ib: sz.decompress(dev, n, dtype, in_bytes=ib),
+           lambda t: O.validate(t, dtype, n),
+           lambda t: O.decompress(t, dtype, n))
+
+
+@pytest.mark.parametrize("variant", [O.SENTINEL, O.TOP8], ids=["sentinel", "top8"])
+@pytest.mark.parametrize("sigma", [1.0, 2.5], ids=["few", "many"])
+def test_variant_decoders_reject_exactly_what_the_oracle_rejects(variant, sigma):
+    n = 3 * 65536 + 4321
+    xh, cb = _data(O.BF16, n, sigma, 4000 if sigma < 2 else 300)
+    good = O.variant_compress(variant, xh, cb)
+    print(f"case fuzz variant={variant} sigma={sigma} escapes={u64(good, 16)}", flush=True)
+    code_bytes = 3 * ((n + 7) // 8) if variant == O.TOP8 else (n + 1) // 2
+    rec = 1 if variant == O.SENTINEL else 3
+    _check(_mutations(good, n, code_bytes, rec, np.random.default_rng(variant * 100 + int(sigma)), 100),
+           lambda dev, ib: sz.variant_decompress(variant, dev, n, in_bytes=ib),
+           lambda t: O.variant_decompress_rc(variant, t, n)[0],
+           lambda t: O.variant_decompress(variant, t, n))
