@@ -148,8 +148,10 @@ const char* splitzip_status_string(int status);
  * (top-15) or 3E (top-8) at the end.  Codebooks are 16 distinct entries per
  * segment as for splitzip_compress; the variant uses the first 15 or 8.
  * The arguments, alignment, workspace and status conventions are those of
- * splitzip_max_compressed_size, splitzip_compress and splitzip_decompress;
- * dtype is BF16.  An invalid variant returns 0 / SPLITZIP_E_INVALID. */
+ * splitzip_max_compressed_size, splitzip_compress and splitzip_decompress,
+ * except that the top-8 workspace stages up to 1024 escape records per
+ * 8192-element tile (4 KiB more per tile than the codec's 512); dtype is
+ * BF16.  An invalid variant returns 0 / SPLITZIP_E_INVALID. */
 typedef enum { SPLITZIP_VARIANT_TOP15_SENTINEL = 1, SPLITZIP_VARIANT_TOP8 = 2 } splitzip_variant;
 
 size_t splitzip_variant_max_compressed_size(int variant, size_t n_elems, uint32_t n_codebooks);

@@ -88,6 +88,11 @@ __host__ __device__ inline Sections sections_of(int dtype, uint64_t n, uint64_t 
   return s;
 }
 
+// Staged escape records per tile in the encoder workspace: enough for the
+// codec's workloads (at most a few percent escapes); the top-8 variant, whose
+// codes miss about 7% of exponents on the same data, gets twice as many.
+__host__ __device__ constexpr uint32_t stage_slot(int variant) { return variant == kTop8 ? 1024u : 512u; }
+
 // Encoder workspace, after the largest possible stream: u64 escapes per
 // block of 64 tiles, u32 escapes per tile, then per tile a staging slot of
 // 512 u32 records.
@@ -114,7 +119,7 @@ __host__ inline Workspace workspace_of(uint8_t* out, int dtype, uint64_t n, uint
   w.tile_count = reinterpret_cast<uint32_t*>(out + at);  // 16-byte loads in encode_sums
   at = round256(at + 4 * tiles);
   w.stage = reinterpret_cast<uint32_t*>(out + at);
-  at += 4 * 512 * tiles;
+  at += 4ull * stage_slot(variant) * tiles;
   w.end = round256(at);
   return w;
 }
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) { prep_work(
 //   encode_dense  one workgroup per 8192-element tile: dense encode (codes,
 //                 sign|mantissa) and element-order escape ranks.  The tile's
 //                 escape count goes to the workspace; when it holds at most
-//                 kStageSlot escapes its records go to the tile's staging
+//                 stage_slot escapes its records go to the tile's staging
 //                 slot.
 //   encode_sums   one thread per block of kBlockTiles tiles: the block's
 //                 escape count.
@@ -272,7 +277,7 @@ struct EncArgs {
   uint64_t n, n_tiles, n_blocks, offsets, nib, sm, esc, chunks;
   uint64_t seg_chunks;    // chunks per codebook segment, 0 when one codebook
   uint32_t* tile_count;   // per tile: escapes in it
-  uint32_t* stage;        // per tile: kStageSlot records (position | exponent << 16)
+  uint32_t* stage;        // per tile: stage_slot(variant) records (position | exponent << 16)
   uint64_t* block_sum;    // per block of kBlockTiles tiles: escapes in it
   uint64_t* super_sum;    // per 64 blocks: escapes in them
   uint64_t* out_bytes;
@@ -283,7 +288,6 @@ struct EncArgs {
   PrepArgs prep;          // the header work folded into a later launch (prep_in 1 or 2)
 };
 
-constexpr uint32_t kStageSlot = 512;  // staged escape records per tile
 
 constexpr uint32_t kBlockTiles = 64;  // tiles per encode_place workgroup
 
@@ -298,7 +302,8 @@ struct EncShared {
   alignas(16) uint32_t s3[4 * 96];  // E5M2: a wave's 64 x 6 sign|mantissa bytes, gathered for aligned stores
 };
 
-static_assert(kStageSlot <= 4 * 256, "staged records reuse the E5M2 table space");
+static_assert(stage_slot(kMain) <= 4 * 256 && stage_slot(kTop8) <= 4 * 256,
+              "staged records reuse the E5M2 table space");
 
 constexpr uint32_t kPlaceRecs = 2048;  // escape records per LDS window of encode_place
 constexpr uint32_t kPlaceWgs = 2048;   // encode_place aims at this many workgroups
@@ -685,7 +690,8 @@ __device__ void encode_dense(const EncArgs& a) {
                         kBf16 ? 256u : 32u);
   const TileEsc r = kBf16 ? encode_tile_bf16<kVariant>(a, sh, t, in, true) : encode_tile_e5m2(a, sh, t, in, true);
   if (threadIdx.x == 0) a.tile_count[t] = r.agg;
-  if (r.agg <= kStageSlot) {  // uniform
+  constexpr uint32_t kSlot = stage_slot(kVariant);
+  if (r.agg <= kSlot) {  // uniform
     // records gathered in LDS first (the E5M2 tables are dead after the
     // rank scan's barrier), then written to the slot with contiguous
     // stores instead of scattered 4-byte ones
@@ -694,7 +700,7 @@ __device__ void encode_dense(const EncArgs& a) {
     if (kBf16) for_each_escape_bf16(a, t, r, stage);
     else for_each_escape_e5m2(a, t, r, stage);
     __syncthreads();
-    uint32_t* slot = a.stage + t * kStageSlot;
+    uint32_t* slot = a.stage + t * kSlot;
     for (uint32_t i = threadIdx.x; i < r.agg; i += kThreads) slot[i] = rec[i];
   }
 }
@@ -792,7 +798,8 @@ __device__ void encode_place(const EncArgs& a) {
   const uint64_t t = t0 + tid;
   const bool mine = tid < tiles;
   const uint32_t cnt = mine ? a.tile_count[t] : 0u;
-  const bool over = cnt > kStageSlot;
+  constexpr uint32_t kSlot = stage_slot(kVariant);
+  const bool over = cnt > kSlot;
 
   // base: the first wave adds the lower blocks of the super-block, the
   // second the lower tiles of the block, all waves the lower super-blocks;
@@ -859,7 +866,7 @@ __device__ void encode_place(const EncArgs& a) {
           else hi = mid;
         }
         const uint32_t r = j - sh.pre_staged[lo];
-        v[u] = a.stage[(t0 + lo) * kStageSlot + r];
+        v[u] = a.stage[(t0 + lo) * kSlot + r];
         dst[u] = base + sh.pre_all[lo] + r;
       }
     }
@@ -878,7 +885,7 @@ __device__ void encode_place(const EncArgs& a) {
   uint64_t table_cb = ~0ull;
   for (uint32_t i = 0; i < tiles; ++i) {
     const uint32_t n_i = sh.pre_all[i + 1] - sh.pre_all[i];
-    if (n_i <= kStageSlot) continue;  // uniform
+    if (n_i <= kSlot) continue;  // uniform
     uint32_t tid_i = tid;
     asm volatile("" : "+v"(tid_i));
     const uint64_t tt = t0 + i;

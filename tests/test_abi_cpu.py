@@ -141,6 +141,9 @@ def test_variant_max_size_and_argument_errors():
         for n, k in [(0, 1), (1, 1), (8191, 1), (1 << 20, 4)]:
             cap = sz.splitzip_variant_max_compressed_size(v, n, k)
             assert cap >= O.variant_max_size(v, n, k) and cap % 256 == 0
+            # the workspace stages up to 512 escape records per 8192-element tile, 1024 for top-8
+            slot = 1024 if v == sz.VARIANT_TOP8 else 512
+            assert cap >= O.variant_max_size(v, n, k) + (4 * slot + 4) * (-(-n // 8192))
     assert sz.splitzip_variant_max_compressed_size(0, 100, 1) == 0
     assert sz.splitzip_variant_max_compressed_size(3, 100, 1) == 0
     lib = sz.load()
