@@ -681,6 +681,25 @@ __device__ inline void put_record(const EncArgs& a, uint64_t index, uint32_t pos
   d[2] = (uint8_t)val;
 }
 
+// Records idx .. idx+3 (idx a multiple of 4, each position | exponent << 16):
+// whole 4-byte words of the escape section, which is 256-aligned -- 3 words
+// of [pos lo, pos hi, exponent] records, or 1 word of exponent bytes with the
+// sentinel variant.
+template <int kVariant = kMain>
+__device__ inline void put_record_group(const EncArgs& a, uint64_t idx, uint32_t r0, uint32_t r1, uint32_t r2,
+                                        uint32_t r3) {
+  if (idx + 4 > a.n) return;  // never taken for a correct scan; keeps stores inside the stream
+  if (kVariant == kSentinel) {
+    *reinterpret_cast<uint32_t*>(a.out + a.esc + idx) =
+        (r0 >> 16) | ((r1 >> 8) & 0xFF00u) | (r2 & 0xFF0000u) | ((r3 << 8) & 0xFF000000u);
+    return;
+  }
+  uint32_t* d = reinterpret_cast<uint32_t*>(a.out + a.esc + 3 * idx);
+  d[0] = (r0 & 0xFFFFFFu) | (r1 << 24);
+  d[1] = ((r1 >> 8) & 0xFFFFu) | (r2 << 16);
+  d[2] = ((r2 >> 16) & 0xFFu) | (r3 << 8);
+}
+
 template <bool kBf16, int kVariant = kMain>
 __device__ void encode_dense(const EncArgs& a) {
   __shared__ EncShared sh;
@@ -760,17 +779,7 @@ __device__ void write_records(const EncArgs& a, const uint32_t* rec, uint64_t d0
   if (tid < m - tail) put_record<kVariant>(a, d0 + tail + tid, rec[tail + tid] & 0xFFFF, rec[tail + tid] >> 16);
   for (uint32_t g = tid; g < groups; g += kThreads) {
     const uint32_t* r = rec + head + 4 * g;
-    const uint32_t r0 = r[0], r1 = r[1], r2 = r[2], r3 = r[3];
-    const uint64_t idx = d0 + head + 4 * (uint64_t)g;
-    if (idx + 4 > a.n) continue;  // never taken for a correct scan; keeps stores inside the stream
-    if (kVariant == kSentinel) {  // exponent bytes only
-      *reinterpret_cast<uint32_t*>(a.out + a.esc + idx) = (r0 >> 16) | ((r1 >> 8) & 0xFF00u) | (r2 & 0xFF0000u) | (r3 << 8 & 0xFF000000u);
-    } else {  // 12 bytes: [pos lo, pos hi, exponent] x 4
-      uint32_t* d = reinterpret_cast<uint32_t*>(a.out + a.esc + 3 * idx);
-      d[0] = (r0 & 0xFFFFFFu) | (r1 << 24);
-      d[1] = ((r1 >> 8) & 0xFFFFu) | (r2 << 16);
-      d[2] = ((r2 >> 16) & 0xFFu) | (r3 << 8);
-    }
+    put_record_group<kVariant>(a, d0 + head + 4 * (uint64_t)g, r[0], r[1], r[2], r[3]);
   }
 }
 
@@ -851,6 +860,41 @@ __device__ void encode_place(const EncArgs& a) {
 
   // staged records of the range, flattened: record j belongs to the tile i
   // with pre_staged[i] <= j < pre_staged[i + 1]
+  auto tile_of = [&](uint32_t j) {
+    uint32_t lo = 0, hi = tiles;  // last i with pre_staged[i] <= j
+    while (hi - lo > 1) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (sh.pre_staged[mid] <= j) lo = mid;
+      else hi = mid;
+    }
+    return lo;
+  };
+  if (!any_over) {  // uniform
+    // the records fill escape indices [base, base + total): a thread takes
+    // 4 of them from an index that is a multiple of 4, which fill whole
+    // words (3, or 1 with the sentinel variant); the few records before the
+    // first and after the last such group are written byte by byte
+    const uint32_t head = std::min<uint32_t>(total, (uint32_t)(-base & 3));
+    const uint32_t groups = (total - head) / 4, tail0 = head + 4 * groups;
+    const uint32_t j_odd = tid < head ? tid : tail0 + (tid - head);  // head then tail records, one per thread
+    if (j_odd < total && (tid < head || tid - head < total - tail0)) {
+      const uint32_t i = tile_of(j_odd);
+      const uint32_t v = a.stage[(t0 + i) * kSlot + (j_odd - sh.pre_staged[i])];
+      put_record<kVariant>(a, base + j_odd, v & 0xFFFF, v >> 16);
+    }
+    for (uint32_t g = tid; g < groups; g += kThreads) {
+      const uint32_t j = head + 4 * g;
+      uint32_t i = tile_of(j);
+      uint32_t v[4];
+#pragma unroll
+      for (uint32_t k = 0; k < 4; ++k) {
+        while (i + 1 < tiles && sh.pre_staged[i + 1] <= j + k) ++i;  // at most a few steps: tiles hold records
+        v[k] = a.stage[(t0 + i) * kSlot + (j + k - sh.pre_staged[i])];
+      }
+      put_record_group<kVariant>(a, base + j, v[0], v[1], v[2], v[3]);
+    }
+    return;
+  }
   for (uint32_t j0 = 0; j0 < staged_total; j0 += kThreads * kPlaceBatch) {
     uint32_t v[kPlaceBatch];
     uint64_t dst[kPlaceBatch];
@@ -859,12 +903,7 @@ __device__ void encode_place(const EncArgs& a) {
       const uint32_t j = j0 + u * kThreads + tid;
       dst[u] = ~0ull;
       if (j < staged_total) {
-        uint32_t lo = 0, hi = tiles;  // last i with pre_staged[i] <= j
-        while (hi - lo > 1) {
-          const uint32_t mid = (lo + hi) >> 1;
-          if (sh.pre_staged[mid] <= j) lo = mid;
-          else hi = mid;
-        }
+        const uint32_t lo = tile_of(j);
         const uint32_t r = j - sh.pre_staged[lo];
         v[u] = a.stage[(t0 + lo) * kSlot + r];
         dst[u] = base + sh.pre_all[lo] + r;
@@ -874,7 +913,6 @@ __device__ void encode_place(const EncArgs& a) {
     for (uint32_t u = 0; u < kPlaceBatch; ++u)
       if (dst[u] != ~0ull) put_record<kVariant>(a, dst[u], v[u] & 0xFFFF, v[u] >> 16);
   }
-  if (!any_over) return;  // uniform
 
   // tiles whose escapes overflowed their slot: encoded again, records in
   // element order through LDS windows to word stores.  The thread index is
