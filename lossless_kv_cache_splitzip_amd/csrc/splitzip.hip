@@ -24,13 +24,15 @@
 //   encode_sums   escape count of each block of 64 tiles.
 //   encode_place  per range of 8 to 64 tiles: base (lower super-blocks,
 //                 blocks and tiles), tile scan, chunk offsets, staged records
-//                 moved to their place through LDS (word stores); tiles whose
-//                 records overflowed their slot are encoded again.
+//                 moved to their place four at a time as whole words; tiles
+//                 whose records overflowed their slot are encoded again and
+//                 written through an LDS window.
 //   decode        one workgroup per tile inside one chunk (8192 BF16 or
-//                 16384 E5M2 elements).  Dense loads go out first; the
-//                 tile's escape records are staged in LDS (bitmap + values),
-//                 from a direct load of a short chunk's records or a 64-way
-//                 wave search of a long one; codes go through an LDS table
+//                 16384 E5M2 elements).  A short chunk's escape records (in
+//                 groups of four, as words), then the dense data, are loaded
+//                 first; the tile's escapes are staged in LDS (bitmap +
+//                 values), after a 64-way wave search for a long chunk's
+//                 records; codes go through an LDS table
 //                 indexed by a whole nibble byte, and escapes are patched in
 //                 registers before non-temporal stores.
 #include <hip/hip_runtime.h>
@@ -66,7 +68,7 @@ __host__ __device__ inline uint64_t round256(uint64_t x) { return (x + 255) & ~u
 __host__ __device__ inline uint64_t divup(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
 // Codebook of chunk c when a segment spans seg_chunks > 0 chunks, in 32-bit
-// arithmetic (c < 2^24 since n <= 2^40); a 64-bit division would cost every
+// arithmetic (c < 2^20 since n <= 2^36); a 64-bit division would cost every
 // wave a long emulation.
 __device__ inline uint32_t codebook_of_chunk(uint64_t c, uint64_t seg_chunks) {
   return seg_chunks > 0xFFFFFFFFull ? 0u : (uint32_t)c / (uint32_t)seg_chunks;
@@ -94,8 +96,8 @@ __host__ __device__ inline Sections sections_of(int dtype, uint64_t n, uint64_t 
 __host__ __device__ constexpr uint32_t stage_slot(int variant) { return variant == kTop8 ? 1024u : 512u; }
 
 // Encoder workspace, after the largest possible stream: u64 escapes per
-// block of 64 tiles, u32 escapes per tile, then per tile a staging slot of
-// 512 u32 records.
+// block of 64 tiles and per super-block of 64 blocks, u32 escapes per tile,
+// then per tile a staging slot of stage_slot(variant) u32 records.
 __host__ __device__ inline uint64_t workspace_offset(int dtype, uint64_t n, uint64_t k, int variant) {
   const Sections s = sections_of(dtype, n, k, variant);
   return round256(s.esc + s.rec * n);
@@ -258,7 +260,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) { prep_work(
 //
 // Three launches (two with at most 64 blocks: no encode_sums); no workgroup
 // waits on another, so no launch needs co-residency:
-//   encode_dense  one workgroup per 8192-element tile: dense encode (codes,
+//   encode_dense  one workgroup per tile (8192 BF16 or 16384 E5M2
+//                 elements): dense encode (codes,
 //                 sign|mantissa) and element-order escape ranks.  The tile's
 //                 escape count goes to the workspace; when it holds at most
 //                 stage_slot escapes its records go to the tile's staging
@@ -268,9 +271,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) { prep_work(
 //   encode_place  one workgroup per range of 8 to 64 tiles (about 2048
 //                 workgroups): the range's base (sum of the lower blocks and
 //                 tiles), scan of its tiles' counts, chunk offsets (E and S
-//                 for the last range), staged records moved to their place;
-//                 a tile whose escapes overflowed its slot is encoded again.
-//                 Records reach the stream through LDS as whole words.
+//                 for the last range), staged records moved to their place
+//                 four at a time as whole words; a tile whose escapes
+//                 overflowed its slot is encoded again and its records go
+//                 through an LDS window, also as whole words.
 struct EncArgs {
   const uint8_t* in;
   uint8_t* out;
@@ -288,8 +292,7 @@ struct EncArgs {
   PrepArgs prep;          // the header work folded into a later launch (prep_in 1 or 2)
 };
 
-
-constexpr uint32_t kBlockTiles = 64;  // tiles per encode_place workgroup
+constexpr uint32_t kBlockTiles = 64;  // tiles per block of the escape-count sums (a placement range lies inside one)
 
 struct EncShared {
   uint8_t table[256];
@@ -540,7 +543,8 @@ __device__ inline bool ranks_miss(uint32_t k, uint32_t count, uint32_t w0, uint3
 
 template <bool kWindow = false, typename Put>
 __device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put,
-                                            uint32_t w0 = 0, uint32_t wlen = 0, uint32_t tid = threadIdx.x, const TileIn* in = nullptr) {
+                                            uint32_t w0 = 0, uint32_t wlen = 0, uint32_t tid = threadIdx.x,
+                                            const TileIn* in = nullptr) {
   const uint16_t* in16 = reinterpret_cast<const uint16_t*>(a.in);
   const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTileBf16;
 #pragma unroll
@@ -553,7 +557,8 @@ __device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, con
     while (m) {
       const uint32_t j = __builtin_ctz(m);
       m &= m - 1;
-      const uint32_t x = in ? pick4(in->w[g].x, in->w[g].y, in->w[g].z, in->w[g].w, j >> 1) >> (16 * (j & 1)) : in16[e0 + j];
+      const uint32_t x =
+          in ? pick4(in->w[g].x, in->w[g].y, in->w[g].z, in->w[g].w, j >> 1) >> (16 * (j & 1)) : in16[e0 + j];
       put(k++, in_chunk + g * 2048 + 8 * tid + j, (x >> 7) & 0xFF);
     }
   }
@@ -651,7 +656,8 @@ __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t ti
 
 template <bool kWindow = false, typename Put>
 __device__ inline void for_each_escape_e5m2(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put,
-                                            uint32_t w0 = 0, uint32_t wlen = 0, uint32_t tid = threadIdx.x, const TileIn* in = nullptr) {
+                                            uint32_t w0 = 0, uint32_t wlen = 0, uint32_t tid = threadIdx.x,
+                                            const TileIn* in = nullptr) {
   const uint32_t in_chunk = (uint32_t)(tile & 3) * (uint32_t)kEncTileE5m2;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -662,7 +668,8 @@ __device__ inline void for_each_escape_e5m2(const EncArgs& a, uint64_t tile, con
     while (m) {
       const uint32_t j = __builtin_ctz(m);
       m &= m - 1;
-      const uint32_t x = in ? pick4(in->w[g].x, in->w[g].y, in->w[g].z, in->w[g].w, j >> 2) >> (8 * (j & 3)) : a.in[e0 + j];
+      const uint32_t x =
+          in ? pick4(in->w[g].x, in->w[g].y, in->w[g].z, in->w[g].w, j >> 2) >> (8 * (j & 3)) : a.in[e0 + j];
       put(k++, in_chunk + g * 4096 + 16 * tid + j, (x >> 2) & 0x1F);
     }
   }
