@@ -29,6 +29,11 @@ namespace {
 constexpr int kHistThreads = 512;
 constexpr uint64_t kElemsPerRange = 65536;  // elements per calib_hist step
 constexpr uint32_t kMaxBlocksPerSeg = 8192;  // workgroups per segment; more ranges loop
+// ranges per workgroup (grid-stride): fewer workgroups clear, reduce and add
+// their histograms (1 -> 4 measured -4% BF16, -7% E5M2 on the 1 and 2.5 GiB caches)
+constexpr uint64_t kRangesPerBlock = 4;
+
+uint64_t divup_u64(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
 __global__ __launch_bounds__(256) void calib_zero_kernel(uint64_t* hist, uint32_t words) {
   const uint32_t i = blockIdx.x * 256 + threadIdx.x;
@@ -117,7 +122,8 @@ int splitzip_calibrate_device(int dtype, const void* d_samples, size_t n_elems, 
     return SPLITZIP_E_INVALID;
   const uint64_t seg = n_codebooks == 1 ? std::max<uint64_t>(n_elems, 1) : segment_elems;
   if (seg == 0 || (uint64_t)n_codebooks * seg < n_elems) return SPLITZIP_E_INVALID;
-  const uint64_t blocks = std::min<uint64_t>(kMaxBlocksPerSeg, (seg + kElemsPerRange - 1) / kElemsPerRange);
+  const uint64_t blocks =
+      std::min<uint64_t>(kMaxBlocksPerSeg, divup_u64(seg, kRangesPerBlock * kElemsPerRange));
   if (work_bytes < need) return SPLITZIP_E_CAPACITY;
   const uint32_t bins = dtype == SPLITZIP_BF16 ? 256 : 32;
   uint64_t* hist = static_cast<uint64_t*>(d_work);
