@@ -142,18 +142,24 @@ def test_segment_codebooks(dtype):
     assert _gpu_roundtrip_ok(out, nb, x, dtype)
 
 
-def test_many_codebooks_multiple_prep_launches():
-    """More codebooks than one prep launch carries (130 > 128)."""
-    K, seg = 130, 65536
+@pytest.mark.parametrize("dtype,K", [(O.BF16, 128), (O.BF16, 130), (O.E5M2, 129)],
+                         ids=["bf16-128", "bf16-130", "e5m2-129"])
+def test_many_codebooks_multiple_prep_launches(dtype, K):
+    """Up to 128 codebooks travel in the kernel arguments; more take header
+    launches of their own (128 per launch) and the tile kernels read the
+    codebooks from the stream."""
+    seg = 65536
     n = K * seg - 999
-    xt = kvsynth.random_bits(n, O.BF16, seed=5)
+    xt = kvsynth.random_bits(n, dtype, seed=5)
     xh = _bits_np(xt)
     rng = np.random.default_rng(2)
-    cbs = np.stack([rng.permutation(np.arange(110, 140))[:16].astype(np.uint8) for _ in range(K)])
+    lo = 110 if dtype == O.BF16 else 6
+    cbs = np.stack([rng.permutation(np.arange(lo, lo + 20))[:16].astype(np.uint8) for _ in range(K)])
     x = xt.to(DEV)
+    _say(f"case dtype={dtype} K={K} n={n}")
     out, nb = _gpu_compress(x, cbs, seg)
-    assert np.array_equal(out[:nb].cpu().numpy(), O.compress(O.BF16, xh, cbs, seg))
-    assert _gpu_roundtrip_ok(out, nb, x, O.BF16)
+    assert np.array_equal(out[:nb].cpu().numpy(), O.compress(dtype, xh, cbs, seg))
+    assert _gpu_roundtrip_ok(out, nb, x, dtype)
 
 
 @pytest.mark.parametrize("dtype", [O.BF16, O.E5M2], ids=["bf16", "e5m2"])
