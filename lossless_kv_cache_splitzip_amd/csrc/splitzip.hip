@@ -20,7 +20,8 @@
 //                 byte permutes (E5M2: one OR of four per-byte-position
 //                 table words per input word), non-temporal lane-contiguous
 //                 stores, element-order escape ranks (wave64 DPP scan +
-//                 LDS), escape records staged per tile in the workspace.
+//                 LDS), escape records staged per tile in the workspace
+//                 (BF16: exponents of escape-dense groups kept in LDS).
 //   encode_sums   escape count of each block of 64 tiles.
 //   encode_place  per range of 8 to 64 tiles: base (lower super-blocks,
 //                 blocks and tiles), tile scan, chunk offsets, staged records
@@ -363,9 +364,10 @@ __device__ inline void build_table(const EncArgs& a, EncShared& sh, uint64_t cbi
 // Per-thread escape bookkeeping of one tile: element-order rank of the
 // thread's first escape in each group, and the escape masks.
 struct TileEsc {
-  uint32_t agg;      // escapes in the tile
-  uint32_t rank[4];  // per group (4 groups: BF16 8 elements per thread, E5M2 16)
-  uint32_t mask[4];  // escaped elements of each group, bit j = element j
+  uint32_t agg;             // escapes in the tile
+  uint32_t lds_groups = 0;  // BF16 dense encode: groups whose exponents went to LDS (bit g; same in a wave)
+  uint32_t rank[4];         // per group (4 groups: BF16 8 elements per thread, E5M2 16)
+  uint32_t mask[4];         // escaped elements of each group, bit j = element j
 };
 
 __device__ inline void wave_totals_to_lds(EncShared& sh, uint32_t i01, uint32_t i23, uint32_t tid) {
@@ -457,9 +459,17 @@ __device__ inline uint32_t codes12(uint32_t w) {
   return (v & 0x3Fu) | ((v >> 10) & 0xFC0u);
 }
 
+// With `exps` (the dense kernel), a group in which at least kLdsLanes of a
+// wave's threads hold escapes has every thread's 8 exponent bytes written to
+// exps[element] and its bit set in lds_groups: the escape pass then reads
+// them from LDS instead of reading the input again.  Few escapes (the common
+// case) skip the writes; many escapes would otherwise cost each wave one
+// dependent global load per escape of a thread.
+constexpr uint32_t kLdsLanes = 4;
+
 template <int kVariant = kMain>
 __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store,
-                                   uint32_t tid = threadIdx.x) {
+                                   uint32_t tid = threadIdx.x, uint8_t* exps = nullptr) {
   const uint32_t lane = tid & 63, wave = tid >> 6;
   const uint64_t first = tile * kEncTileBf16;
   const bool tile_full = first + kEncTileBf16 <= a.n;  // same in every thread
@@ -483,6 +493,12 @@ __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t ti
     const uint32_t f = ((lo >> 4) & 0x01010101u) | ((hi >> 3) & 0x02020202u);
     r.mask[g] = f;
     cnt[g] = __builtin_popcount(f);
+    if (exps && __popcll(__ballot(f != 0)) >= kLdsLanes) {  // same in the wave
+      r.lds_groups |= 1u << g;
+      const uint32_t e03 = perm((x.y >> 7) & 0x00FF00FFu, (x.x >> 7) & 0x00FF00FFu, 0x06040200u);
+      const uint32_t e47 = perm((x.w >> 7) & 0x00FF00FFu, (x.z >> 7) & 0x00FF00FFu, 0x06040200u);
+      *reinterpret_cast<uint2*>(exps + local) = make_uint2(e03, e47);
+    }
     if (store) {
       // sign|mantissa: high bytes and low bytes of the four BF16 pairs
       const uint32_t h01 = perm(x.y, x.x, 0x07050301u), l01 = perm(x.y, x.x, 0x06040200u);
@@ -530,35 +546,71 @@ __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t ti
 }
 
 // The escapes of one BF16 tile: position in chunk and raw exponent, handed
-// to `put(rank, pos, exponent)` in element order.  The exponent is read again
-// from the input, or, when `in` is given, taken from the tile's registers
-// (the dense kernel reads it again: keeping the input registers live there
-// measured slower; the re-encode of an escape-heavy tile takes it from
-// registers).  With kWindow, only ranks in [w0, w0 + wlen) are wanted: a
-// thread's escapes of one group have consecutive ranks, and groups whose
-// ranks all miss the window are skipped.
+// to `put(rank, pos, exponent)` in element order (a thread's escapes of one
+// group have consecutive ranks).
+//
+// Dense kernel: the exponents of LDS groups (lds_groups) come from `exps`;
+// the others are read again from the input, the first escape of each of the
+// four groups with loads issued together (keeping the input registers live
+// through the rank scan instead measured slower).
+template <typename Put>
+__device__ inline void dense_escapes_bf16(const EncArgs& a, uint64_t tile, const TileEsc& r, const uint8_t* exps,
+                                          Put put) {
+  const uint32_t tid = threadIdx.x;
+  const uint16_t* in16 = reinterpret_cast<const uint16_t*>(a.in) + tile * kEncTileBf16;
+  const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTileBf16;
+  uint32_t m[4], x0[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t f = r.mask[g];  // element k at bit 8k, element 4 + k at bit 8k + 1
+    m[g] = f ? flag_mask4(f << 4) | (flag_mask4(f << 3) << 4) : 0u;  // element order
+    if (m[g] && !((r.lds_groups >> g) & 1)) x0[g] = in16[g * 2048 + 8 * tid + __builtin_ctz(m[g])];
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    uint32_t mg = m[g], k = r.rank[g];
+    if (!mg) continue;
+    const uint32_t local = g * 2048 + 8 * tid;
+    if ((r.lds_groups >> g) & 1) {  // same in the wave
+      const uint2 e = *reinterpret_cast<const uint2*>(exps + local);
+      while (mg) {
+        const uint32_t j = __builtin_ctz(mg);
+        mg &= mg - 1;
+        put(k++, in_chunk + local + j, ((j < 4 ? e.x : e.y) >> (8 * (j & 3))) & 0xFF);
+      }
+    } else {
+      uint32_t x = x0[g];
+      while (mg) {
+        const uint32_t j = __builtin_ctz(mg);
+        mg &= mg - 1;
+        put(k++, in_chunk + local + j, (x >> 7) & 0xFF);
+        if (mg) x = in16[local + __builtin_ctz(mg)];
+      }
+    }
+  }
+}
+
+// Re-encode of a tile that overflowed its slot: exponents from the tile's
+// registers, and only ranks in [w0, w0 + wlen) are wanted (groups whose
+// ranks all miss the window are skipped).
 __device__ inline bool ranks_miss(uint32_t k, uint32_t count, uint32_t w0, uint32_t wlen) {
   return k + count <= w0 || (k >= w0 && k - w0 >= wlen);
 }
 
-template <bool kWindow = false, typename Put>
-__device__ inline void for_each_escape_bf16(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put,
-                                            uint32_t w0 = 0, uint32_t wlen = 0, uint32_t tid = threadIdx.x,
-                                            const TileIn* in = nullptr) {
-  const uint16_t* in16 = reinterpret_cast<const uint16_t*>(a.in);
+template <typename Put>
+__device__ inline void window_escapes_bf16(uint64_t tile, const TileEsc& r, const TileIn& in, uint32_t w0,
+                                           uint32_t wlen, uint32_t tid, Put put) {
   const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTileBf16;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const uint32_t f = r.mask[g];  // element k at bit 8k, element 4 + k at bit 8k + 1
-    uint32_t m = f ? flag_mask4(f << 4) | (flag_mask4(f << 3) << 4) : 0u;  // element order
+    const uint32_t f = r.mask[g];
+    uint32_t m = f ? flag_mask4(f << 4) | (flag_mask4(f << 3) << 4) : 0u;
     uint32_t k = r.rank[g];
-    if (kWindow && ranks_miss(k, __builtin_popcount(m), w0, wlen)) continue;
-    const uint64_t e0 = tile * kEncTileBf16 + g * 2048 + 8 * tid;
+    if (ranks_miss(k, __builtin_popcount(m), w0, wlen)) continue;
     while (m) {
       const uint32_t j = __builtin_ctz(m);
       m &= m - 1;
-      const uint32_t x =
-          in ? pick4(in->w[g].x, in->w[g].y, in->w[g].z, in->w[g].w, j >> 1) >> (16 * (j & 1)) : in16[e0 + j];
+      const uint32_t x = pick4(in.w[g].x, in.w[g].y, in.w[g].z, in.w[g].w, j >> 1) >> (16 * (j & 1));
       put(k++, in_chunk + g * 2048 + 8 * tid + j, (x >> 7) & 0xFF);
     }
   }
@@ -654,22 +706,43 @@ __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t ti
   return r;
 }
 
-template <bool kWindow = false, typename Put>
-__device__ inline void for_each_escape_e5m2(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put,
-                                            uint32_t w0 = 0, uint32_t wlen = 0, uint32_t tid = threadIdx.x,
-                                            const TileIn* in = nullptr) {
+// The escapes of one E5M2 tile, as dense_escapes_bf16 / window_escapes_bf16
+// (the dense kernel reads every exponent again from the input).
+template <typename Put>
+__device__ inline void dense_escapes_e5m2(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put) {
+  const uint32_t tid = threadIdx.x;
+  const uint8_t* in8 = a.in + tile * kEncTileE5m2;
+  const uint32_t in_chunk = (uint32_t)(tile & 3) * (uint32_t)kEncTileE5m2;
+  uint32_t x0[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    if (r.mask[g]) x0[g] = in8[g * 4096 + 16 * tid + __builtin_ctz(r.mask[g])];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    uint32_t m = r.mask[g], k = r.rank[g], x = x0[g];
+    const uint32_t local = g * 4096 + 16 * tid;
+    while (m) {
+      const uint32_t j = __builtin_ctz(m);
+      m &= m - 1;
+      put(k++, in_chunk + local + j, (x >> 2) & 0x1F);
+      if (m) x = in8[local + __builtin_ctz(m)];
+    }
+  }
+}
+
+template <typename Put>
+__device__ inline void window_escapes_e5m2(uint64_t tile, const TileEsc& r, const TileIn& in, uint32_t w0,
+                                           uint32_t wlen, uint32_t tid, Put put) {
   const uint32_t in_chunk = (uint32_t)(tile & 3) * (uint32_t)kEncTileE5m2;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     uint32_t m = r.mask[g];
     uint32_t k = r.rank[g];
-    if (kWindow && ranks_miss(k, __builtin_popcount(m), w0, wlen)) continue;
-    const uint64_t e0 = tile * kEncTileE5m2 + g * 4096 + 16 * tid;
+    if (ranks_miss(k, __builtin_popcount(m), w0, wlen)) continue;
     while (m) {
       const uint32_t j = __builtin_ctz(m);
       m &= m - 1;
-      const uint32_t x =
-          in ? pick4(in->w[g].x, in->w[g].y, in->w[g].z, in->w[g].w, j >> 2) >> (8 * (j & 3)) : a.in[e0 + j];
+      const uint32_t x = pick4(in.w[g].x, in.w[g].y, in.w[g].z, in.w[g].w, j >> 2) >> (8 * (j & 3));
       put(k++, in_chunk + g * 4096 + 16 * tid + j, (x >> 2) & 0x1F);
     }
   }
@@ -710,11 +783,13 @@ __device__ inline void put_record_group(const EncArgs& a, uint64_t idx, uint32_t
 template <bool kBf16, int kVariant = kMain>
 __device__ void encode_dense(const EncArgs& a) {
   __shared__ EncShared sh;
+  __shared__ alignas(8) uint8_t exps[kBf16 ? kEncTileBf16 : 8];  // BF16: exponents of LDS groups, by element
   const uint64_t t = blockIdx.x;
   const TileIn in = kBf16 ? load_tile_bf16(a, t) : load_tile_e5m2(a, t);  // in flight during the table build
   build_table<kVariant>(a, sh, a.seg_chunks ? codebook_of_chunk(t >> (kBf16 ? 3 : 2), a.seg_chunks) : 0,
                         kBf16 ? 256u : 32u);
-  const TileEsc r = kBf16 ? encode_tile_bf16<kVariant>(a, sh, t, in, true) : encode_tile_e5m2(a, sh, t, in, true);
+  const TileEsc r =
+      kBf16 ? encode_tile_bf16<kVariant>(a, sh, t, in, true, threadIdx.x, exps) : encode_tile_e5m2(a, sh, t, in, true);
   if (threadIdx.x == 0) a.tile_count[t] = r.agg;
   constexpr uint32_t kSlot = stage_slot(kVariant);
   if (r.agg <= kSlot) {  // uniform
@@ -723,8 +798,8 @@ __device__ void encode_dense(const EncArgs& a) {
     // stores instead of scattered 4-byte ones
     uint32_t* rec = sh.pos4;
     auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) { rec[k] = pos | (val << 16); };
-    if (kBf16) for_each_escape_bf16(a, t, r, stage);
-    else for_each_escape_e5m2(a, t, r, stage);
+    if (kBf16) dense_escapes_bf16(a, t, r, exps, stage);
+    else dense_escapes_e5m2(a, t, r, stage);
     __syncthreads();
     uint32_t* slot = a.stage + t * kSlot;
     for (uint32_t i = threadIdx.x; i < r.agg; i += kThreads) slot[i] = rec[i];
@@ -946,8 +1021,8 @@ __device__ void encode_place(const EncArgs& a) {
       auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) {
         if (k - w0 < kPlaceRecs) sh.rec[k - w0] = pos | (val << 16);
       };
-      if (kBf16) for_each_escape_bf16<true>(a, tt, r, stage, w0, kPlaceRecs, tid_i, &in);
-      else for_each_escape_e5m2<true>(a, tt, r, stage, w0, kPlaceRecs, tid_i, &in);
+      if (kBf16) window_escapes_bf16(tt, r, in, w0, kPlaceRecs, tid_i, stage);
+      else window_escapes_e5m2(tt, r, in, w0, kPlaceRecs, tid_i, stage);
       __syncthreads();
       write_records<kVariant>(a, sh.rec, base + sh.pre_all[i] + w0, std::min<uint32_t>(kPlaceRecs, n_i - w0), tid_i);
       __syncthreads();  // sh.rec and esh are reused
