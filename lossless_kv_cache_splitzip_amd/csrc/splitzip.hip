@@ -1147,15 +1147,17 @@ __device__ inline RecGroup load_rec_group(const DecArgs& a, uint64_t esc, uint64
   return g;
 }
 
-constexpr uint32_t kScanGroups = 1;  // record groups per thread and step of a long chunk (more cost occupancy)
+constexpr uint32_t kScanGroups = 1;   // record groups per thread and step of a long chunk (more cost occupancy)
+constexpr uint32_t kShortGroups = 2;  // record groups per thread of a short chunk (3 cost occupancy)
 
-// The tile's chunk's record range and, for a short chunk (at most kThreads
-// record groups), this thread's group: read before the tile's dense loads
-// are issued, so that waiting for the records does not mean waiting for the
-// dense data queued behind them (loads complete in issue order).
+// The tile's chunk's record range and, for a short chunk (at most
+// kShortGroups * kThreads record groups, 2048 records), this thread's
+// groups: read before the tile's dense loads are issued, so that waiting for
+// the records does not mean waiting for the dense data queued behind them
+// (loads complete in issue order).
 struct EscFetch {
-  uint64_t lo, hi;  // the chunk's records (offsets table)
-  RecGroup G;       // group lo / 4 + thread index, short chunk only
+  uint64_t lo, hi;           // the chunk's records (offsets table)
+  RecGroup G[kShortGroups];  // groups lo / 4 + k * kThreads + thread index, short chunk only
 };
 
 template <uint32_t kDecTile>
@@ -1168,7 +1170,11 @@ __device__ inline EscFetch fetch_escapes(const DecArgs& a, const Header& h, uint
   const uint64_t g_lo = f.lo / 4, g_hi = (f.hi + 3) / 4;
   const uint64_t g = g_lo + threadIdx.x;
   // an inconsistent range is rejected by stage_escapes; nothing is read for it
-  if (f.lo <= f.hi && f.hi <= h.e && g_hi - g_lo <= kThreads && g < g_hi) f.G = load_rec_group(a, h.s.esc, g);
+  if (f.lo <= f.hi && f.hi <= h.e && g_hi - g_lo <= kShortGroups * kThreads) {
+#pragma unroll
+    for (uint32_t k = 0; k < kShortGroups; ++k)
+      if (g + k * kThreads < g_hi) f.G[k] = load_rec_group(a, h.s.esc, g + k * kThreads);
+  }
   return f;
 }
 
@@ -1219,18 +1225,19 @@ __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, 
   };
 
   const uint64_t g_lo = lo / 4, g_hi = (hi + 3) / 4;  // record groups of the chunk
-  if (g_hi - g_lo <= kThreads) {  // uniform
-    // short chunk (up to 1024 records): every tile of the chunk has loaded
-    // all of its records, a group per thread (no search, whose dependent
+  if (g_hi - g_lo <= kShortGroups * kThreads) {  // uniform
+    // short chunk (up to 2048 records): every tile of the chunk has loaded
+    // all of its records, two groups per thread (no search, whose dependent
     // loads would lengthen the tile's critical path); it checks all of them
     // and stages those in its window
     const uint64_t g = g_lo + tid;
-    const RecGroup& G = f.G;
     for (uint32_t i = tid; i < kDecTile / 32; i += kThreads) bitmap[i] = 0;
     if (tid == 0) *s_err = 0;
     __syncthreads();
     bool bad = false;
-    if (g < g_hi) check_group(g, lo, hi, 0, (uint32_t)chunk_len, G, bad);
+#pragma unroll
+    for (uint32_t k = 0; k < kShortGroups; ++k)
+      if (g + k * kThreads < g_hi) check_group(g + k * kThreads, lo, hi, 0, (uint32_t)chunk_len, f.G[k], bad);
     if (bad) *s_err = 1;
     __syncthreads();
     return *s_err == 0;

@@ -5,8 +5,9 @@ the GPU (d_status = E_CORRUPT) exactly when the oracle's validation rejects
 them; a damaged stream that is still valid (another code, an escape moved to
 another free position, an exponent replaced by another in range) decodes to
 the oracle's result bit for bit.  Short chunks (the decoder loads all of a
-chunk's records in every tile) and long chunks (it searches for the tile's
-records) are both covered, for BF16 and E5M2, and so are the two ablation
+chunk's records in every tile: one group of four records per thread up to
+1024 records, two up to 2048) and long chunks (it searches for the tile's
+records) are all covered, for BF16 and E5M2, and so are the two ablation
 variants' decoders.
 """
 import numpy as np
@@ -94,11 +95,14 @@ def _check(cases, gpu_decode, oracle_status, oracle_decode):
 
 
 CASES = [
-    # (dtype, n, data sigma, calibration sample): short chunks, then long ones
-    (O.BF16, 4 * 65536 + 123, 1.0, 4000),
-    (O.BF16, 3 * 65536 + 5001, 2.5, 300),
-    (O.E5M2, 4 * 65536 + 77, 1.0, 4000),
-    (O.E5M2, 2 * 65536 + 999, 3.0, 300),
+    # (dtype, n, data sigma, calibration sample, most records in a chunk: (lo, hi]):
+    # short chunks of one and two record groups per thread, then long ones
+    (O.BF16, 4 * 65536 + 123, 1.0, 4000, (0, 1024)),
+    (O.BF16, 3 * 65536 + 777, 2.0, 300, (1024, 2048)),
+    (O.BF16, 3 * 65536 + 5001, 2.5, 300, (2048, 65536)),
+    (O.E5M2, 4 * 65536 + 77, 1.0, 4000, (0, 1024)),
+    (O.E5M2, 3 * 65536 + 555, 1.8, 300, (1024, 2048)),
+    (O.E5M2, 2 * 65536 + 999, 3.0, 300, (2048, 65536)),
 ]
 
 
@@ -107,18 +111,16 @@ def _data(dtype, n, sigma, calib):
     return xh, O.calibrate(dtype, xh[:calib])
 
 
-@pytest.mark.parametrize("dtype,n,sigma,calib", CASES,
-                         ids=["bf16-short", "bf16-long", "e5m2-short", "e5m2-long"])
-def test_gpu_rejects_exactly_what_the_oracle_rejects(dtype, n, sigma, calib):
+@pytest.mark.parametrize("dtype,n,sigma,calib,most", CASES,
+                         ids=["bf16-short", "bf16-short2", "bf16-long", "e5m2-short", "e5m2-short2", "e5m2-long"])
+def test_gpu_rejects_exactly_what_the_oracle_rejects(dtype, n, sigma, calib, most):
     xh, cb = _data(dtype, n, sigma, calib)
     good = O.compress(dtype, xh, cb)
     E = u64(good, 16)
-    per_chunk = E / max(1, (n + 65535) // 65536)
-    print(f"case fuzz dtype={dtype} n={n} escapes={E} ({per_chunk:.0f} per chunk)", flush=True)
-    if sigma > 2:
-        assert per_chunk > 1024  # the decoder's long-chunk path
-    else:
-        assert 0 < per_chunk <= 1024
+    C = (n + 65535) // 65536
+    per_chunk = [u64(good, 80 + 8 * (c + 1)) - u64(good, 80 + 8 * c) for c in range(C)]
+    print(f"case fuzz dtype={dtype} n={n} escapes={E} per chunk {per_chunk}", flush=True)
+    assert most[0] < max(per_chunk) <= most[1]  # the decoder path the case is for
     code_bytes = (n + 1) // 2
     _check(_mutations(good, n, code_bytes, 3, np.random.default_rng(n), 140),
            lambda dev, ib: sz.decompress(dev, n, dtype, in_bytes=ib),
@@ -127,7 +129,7 @@ def test_gpu_rejects_exactly_what_the_oracle_rejects(dtype, n, sigma, calib):
 
 
 @pytest.mark.parametrize("variant", [O.SENTINEL, O.TOP8], ids=["sentinel", "top8"])
-@pytest.mark.parametrize("sigma", [1.0, 2.5], ids=["few", "many"])
+@pytest.mark.parametrize("sigma", [0.3, 1.0, 2.5], ids=["narrow", "few", "many"])  # top-8 chunks: ~1700, ~4300, ~20700 records
 def test_variant_decoders_reject_exactly_what_the_oracle_rejects(variant, sigma):
     n = 3 * 65536 + 4321
     xh, cb = _data(O.BF16, n, sigma, 4000 if sigma < 2 else 300)
