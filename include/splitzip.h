@@ -19,6 +19,11 @@
  *     nothing.  A failed kernel launch returns SPLITZIP_E_HIP.
  *   - Calls on different streams may run concurrently when their buffers are
  *     disjoint; the library keeps no mutable global state.
+ *   - The device calls (compress, decompress and their variants, the device
+ *     calibration) only launch kernels on `stream`: no allocation, memset or
+ *     synchronization, so they can be captured in a HIP graph and replayed.
+ *     Decompress takes in_bytes as an upper bound (the buffer's size), so a
+ *     captured decompress serves streams of any size S <= in_bytes.
  *
  * Stream format "SZ1" (little-endian; A(x) = x rounded up to a multiple of
  * 256; n elements, C = ceil(n / 65536) chunks, K codebooks, E escapes):
