@@ -340,6 +340,8 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1),
                     help="host threads of the parallel oracle run (the box grants 16)")
     ap.add_argument("--no-link", action="store_true", help="skip the pipelined host-link transfer leg")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the one-layer graph leg (its calls launch the same kernels on a 4 MiB input)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this codec benchmark runs on one GPU; multi-GPU runs are not part of it",
@@ -444,9 +446,10 @@ def main():
     if link:
         log(f"[bench] link: raw {link['raw_ms']:.2f} ms, compressed {link['compressed_ms']:.2f} ms, "
             f"speedup {link['speedup']:.3f}")
-    layer = per_layer_graph_leg()
-    log(f"[bench] one-layer calls: eager {layer['eager_encode_us']:.1f} / {layer['eager_decode_us']:.1f} us, "
-        f"graph-replayed {layer['graph_encode_us']:.1f} / {layer['graph_decode_us']:.1f} us (encode / decode)")
+    layer = None if args.no_layer else per_layer_graph_leg()
+    if layer:
+        log(f"[bench] one-layer calls: eager {layer['eager_encode_us']:.1f} / {layer['eager_decode_us']:.1f} us, "
+            f"graph-replayed {layer['graph_encode_us']:.1f} / {layer['graph_decode_us']:.1f} us (encode / decode)")
     cpu, cpu_par = cpu_baseline(args.workload, args.cpu_budget, args.cpu_threads) if args.cpu_budget > 0 else (None, None)
 
     line = {

@@ -1117,7 +1117,11 @@ struct RecGroup {
   uint32_t prev_pos;  // position of record 4q-1 (0 for q == 0)
 };
 
-__device__ inline RecGroup load_rec_group(const DecArgs& a, uint64_t esc, uint64_t q) {
+struct RecWords {  // words 3q-1 .. 3q+2 as loaded (w0 = 0 for q == 0)
+  uint32_t w0, w1, w2, w3;
+};
+
+__device__ inline RecWords load_rec_words(const DecArgs& a, uint64_t esc, uint64_t q) {
   const uint64_t b = esc + 12 * q;
   uint32_t w0 = 0, w1, w2, w3;
   if (b + 12 <= a.in_bytes) {
@@ -1134,6 +1138,11 @@ __device__ inline RecGroup load_rec_group(const DecArgs& a, uint64_t esc, uint64
     w2 = w[1];
     w3 = w[2];
   }
+  return RecWords{w0, w1, w2, w3};
+}
+
+__device__ inline RecGroup unpack_rec_group(const RecWords& w) {
+  const uint32_t w0 = w.w0, w1 = w.w1, w2 = w.w2, w3 = w.w3;
   RecGroup g;
   g.pos[0] = w1 & 0xFFFFu;
   g.val[0] = (w1 >> 16) & 0xFFu;
@@ -1147,17 +1156,22 @@ __device__ inline RecGroup load_rec_group(const DecArgs& a, uint64_t esc, uint64
   return g;
 }
 
+__device__ inline RecGroup load_rec_group(const DecArgs& a, uint64_t esc, uint64_t q) {
+  return unpack_rec_group(load_rec_words(a, esc, q));
+}
+
 constexpr uint32_t kScanGroups = 1;   // record groups per thread and step of a long chunk (more cost occupancy)
-constexpr uint32_t kShortGroups = 2;  // record groups per thread of a short chunk (3 cost occupancy)
+constexpr uint32_t kShortGroups = 2;  // record groups per thread of a short chunk
 
 // The tile's chunk's record range and, for a short chunk (at most
 // kShortGroups * kThreads record groups, 2048 records), this thread's
-// groups: read before the tile's dense loads are issued, so that waiting for
-// the records does not mean waiting for the dense data queued behind them
-// (loads complete in issue order).
+// groups: loaded before the tile's dense loads are issued, so that waiting
+// for the records does not mean waiting for the dense data queued behind
+// them (loads complete in issue order).  The words are kept as loaded and
+// unpacked by stage_escapes, after the dense loads have been issued.
 struct EscFetch {
   uint64_t lo, hi;           // the chunk's records (offsets table)
-  RecGroup G[kShortGroups];  // groups lo / 4 + k * kThreads + thread index, short chunk only
+  RecWords W[kShortGroups];  // groups lo / 4 + k * kThreads + thread index, short chunk only
 };
 
 template <uint32_t kDecTile>
@@ -1173,7 +1187,7 @@ __device__ inline EscFetch fetch_escapes(const DecArgs& a, const Header& h, uint
   if (f.lo <= f.hi && f.hi <= h.e && g_hi - g_lo <= kShortGroups * kThreads) {
 #pragma unroll
     for (uint32_t k = 0; k < kShortGroups; ++k)
-      if (g + k * kThreads < g_hi) f.G[k] = load_rec_group(a, h.s.esc, g + k * kThreads);
+      if (g + k * kThreads < g_hi) f.W[k] = load_rec_words(a, h.s.esc, g + k * kThreads);
   }
   return f;
 }
@@ -1237,7 +1251,8 @@ __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, 
     bool bad = false;
 #pragma unroll
     for (uint32_t k = 0; k < kShortGroups; ++k)
-      if (g + k * kThreads < g_hi) check_group(g + k * kThreads, lo, hi, 0, (uint32_t)chunk_len, f.G[k], bad);
+      if (g + k * kThreads < g_hi)
+        check_group(g + k * kThreads, lo, hi, 0, (uint32_t)chunk_len, unpack_rec_group(f.W[k]), bad);
     if (bad) *s_err = 1;
     __syncthreads();
     return *s_err == 0;
