@@ -10,6 +10,10 @@
  *   - a stream with a damaged magic number sets d_status to E_CORRUPT;
  *   - host-detectable errors (small output, null input, bad codebook) return
  *     their codes.
+ * Then, on BF16 data, the other entry points from plain C: the device
+ * calibration equals the host one, both ablation variants round-trip, and
+ * the chunk-pipelined transfer through pinned host memory (four streams)
+ * delivers the input with fewer bytes over the link than raw.
  * Exit status 0 when every check holds.  Test infrastructure only.
  */
 #include <hip/hip_runtime_api.h>
@@ -144,8 +148,117 @@ static void run(int dtype, size_t n) {
   free(y);
 }
 
+/* BF16 values with a concentrated exponent distribution (as run()) */
+static uint16_t* bf16_data(size_t n) {
+  uint16_t* x = (uint16_t*)malloc(n * 2);
+  CHECK(x != NULL, "malloc");
+  for (size_t i = 0; i < n; ++i) {
+    const uint64_t r = next64();
+    const uint32_t e = 110 + (uint32_t)__builtin_popcountll(r & 0xFFFFFF);
+    x[i] = (uint16_t)(((r >> 32) & 0x807F) | (e << 7));
+  }
+  return x;
+}
+
+static void extras(void) {
+  const size_t n = 5 * 65536 + 777;
+  uint16_t* x = bf16_data(n);
+  uint16_t* y = (uint16_t*)malloc(n * 2);
+  CHECK(y != NULL, "malloc");
+  void *d_in, *d_y;
+  int32_t* d_status;
+  uint64_t* d_bytes;
+  HIP(hipMalloc(&d_in, n * 2));
+  HIP(hipMalloc(&d_y, n * 2));
+  HIP(hipMalloc((void**)&d_status, 4));
+  HIP(hipMalloc((void**)&d_bytes, 8));
+  HIP(hipMemcpy(d_in, x, n * 2, hipMemcpyHostToDevice));
+
+  /* device calibration of the whole tensor equals the host routine */
+  uint8_t cb[16], cb_dev[16];
+  CHECK(splitzip_calibrate(SPLITZIP_BF16, x, n, cb) == SPLITZIP_OK, "calibrate");
+  const size_t work_bytes = splitzip_calibrate_device_work_bytes(SPLITZIP_BF16, 1);
+  CHECK(work_bytes > 0, "calibrate work bytes");
+  void* d_work;
+  uint8_t* d_cb;
+  HIP(hipMalloc(&d_work, work_bytes));
+  HIP(hipMalloc((void**)&d_cb, 16));
+  CHECK(splitzip_calibrate_device(SPLITZIP_BF16, d_in, n, 0, 1, d_cb, d_work, work_bytes, NULL) == SPLITZIP_OK,
+        "calibrate_device");
+  HIP(hipMemcpy(cb_dev, d_cb, 16, hipMemcpyDeviceToHost));
+  CHECK(memcmp(cb, cb_dev, 16) == 0, "device codebook differs from the host one");
+  HIP(hipFree(d_work));
+  HIP(hipFree(d_cb));
+
+  /* both ablation variants round-trip */
+  const int variants[2] = {SPLITZIP_VARIANT_TOP15_SENTINEL, SPLITZIP_VARIANT_TOP8};
+  for (int v = 0; v < 2; ++v) {
+    const size_t cap = splitzip_variant_max_compressed_size(variants[v], n, 1);
+    CHECK(cap > 0, "variant max size");
+    void* d_out;
+    HIP(hipMalloc(&d_out, cap));
+    HIP(hipMemset(d_status, 0, 4));
+    CHECK(splitzip_variant_compress(variants[v], d_in, n, cb, 1, 0, d_out, cap, d_bytes, NULL) == SPLITZIP_OK,
+          "variant compress");
+    uint64_t S = 0;
+    HIP(hipMemcpy(&S, d_bytes, 8, hipMemcpyDeviceToHost));
+    CHECK(S > 0 && S <= cap, "variant stream size %llu", (unsigned long long)S);
+    CHECK(splitzip_variant_decompress(variants[v], d_out, S, n, d_y, d_status, NULL) == SPLITZIP_OK,
+          "variant decompress");
+    int32_t status = -1;
+    HIP(hipMemcpy(y, d_y, n * 2, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(&status, d_status, 4, hipMemcpyDeviceToHost));
+    CHECK(status == SPLITZIP_OK && memcmp(x, y, n * 2) == 0, "variant %d round trip", variants[v]);
+    printf("c-abi ok: variant=%d n=%zu stream=%llu B\n", variants[v], n, (unsigned long long)S);
+    HIP(hipFree(d_out));
+  }
+
+  /* chunk-pipelined transfer through pinned host memory */
+  const size_t group = 2 * 65536;
+  const uint32_t depth = 4;
+  size_t dw = 0, hl = 0;
+  CHECK(splitzip_pipeline_sizes(SPLITZIP_BF16, n, 1, 0, group, depth, &dw, &hl) == SPLITZIP_OK, "pipeline sizes");
+  void *d_pw, *h_link;
+  HIP(hipMalloc(&d_pw, dw));
+  HIP(hipHostMalloc(&h_link, hl, hipHostMallocCoherent));
+  hipStream_t st[4];
+  for (int i = 0; i < 4; ++i) HIP(hipStreamCreate(&st[i]));
+  const size_t groups = (n + group - 1) / group;
+  uint64_t sent[8] = {0};
+  CHECK(groups <= 8, "groups");
+  HIP(hipMemset(d_y, 0, n * 2));
+  HIP(hipMemset(d_status, 0, 4));
+  HIP(hipDeviceSynchronize());
+  CHECK(splitzip_pipeline_transfer(SPLITZIP_BF16, d_in, n, cb, 1, 0, group, depth, 1, d_pw, dw, h_link, hl, d_y,
+                                   d_status, sent, st) == SPLITZIP_OK,
+        "pipeline transfer");
+  int32_t status = -1;
+  HIP(hipMemcpy(y, d_y, n * 2, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(&status, d_status, 4, hipMemcpyDeviceToHost));
+  CHECK(status == SPLITZIP_OK && memcmp(x, y, n * 2) == 0, "pipeline output differs");
+  uint64_t total = 0;
+  for (size_t g = 0; g < groups; ++g) total += sent[g];
+  CHECK(total > 0 && total < n * 2, "bytes over the link %llu of %zu", (unsigned long long)total, n * 2);
+  printf("c-abi ok: pipeline n=%zu groups=%zu link bytes=%llu (raw %zu)\n", n, groups, (unsigned long long)total,
+         n * 2);
+  for (int i = 0; i < 4; ++i) HIP(hipStreamDestroy(st[i]));
+  HIP(hipHostFree(h_link));
+  HIP(hipFree(d_pw));
+
+  const char* msg = splitzip_status_string(SPLITZIP_E_CORRUPT);
+  CHECK(msg != NULL && msg[0] != 0, "status string");
+  fflush(stdout);
+  HIP(hipFree(d_in));
+  HIP(hipFree(d_y));
+  HIP(hipFree(d_status));
+  HIP(hipFree(d_bytes));
+  free(x);
+  free(y);
+}
+
 int main(void) {
   run(SPLITZIP_BF16, 3 * 65536 + 12345);
   run(SPLITZIP_FP8_E5M2, 5 * 65536 + 777);
+  extras();
   return 0;
 }

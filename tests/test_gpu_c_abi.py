@@ -1,7 +1,9 @@
 """The C ABI used from plain C (tests/c_abi/roundtrip.c, built by
 __graft_entry__.build()): hipMalloc'd buffers, the default stream, no Python
 or PyTorch in the process.  BF16 and E5M2 round trips, the closed-form stream
-size, the corrupt-stream status and host-detectable errors."""
+size, the corrupt-stream status and host-detectable errors; then the device
+calibration against the host one, both ablation variants, and the
+chunk-pipelined transfer through pinned host memory on four streams."""
 import os
 import subprocess
 
@@ -19,4 +21,4 @@ def test_plain_c_round_trip():
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stderr
     lines = [l for l in r.stdout.splitlines() if l.startswith("c-abi ok:")]
-    assert len(lines) == 2
+    assert len(lines) == 5
