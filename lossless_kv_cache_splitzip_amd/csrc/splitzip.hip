@@ -21,7 +21,8 @@
 //                 table words per input word), non-temporal lane-contiguous
 //                 stores, element-order escape ranks (wave64 DPP scan +
 //                 LDS), escape records staged per tile in the workspace
-//                 (BF16: exponents of escape-dense groups kept in LDS).
+//                 (BF16: input read once with non-temporal loads, the
+//                 exponents of groups with escapes kept in LDS).
 //   encode_sums   escape count of each block of 64 tiles.
 //   encode_place  per range of 8 to 64 tiles: base (lower super-blocks,
 //                 blocks and tiles), tile scan, chunk offsets, staged records
@@ -364,10 +365,9 @@ __device__ inline void build_table(const EncArgs& a, EncShared& sh, uint64_t cbi
 // Per-thread escape bookkeeping of one tile: element-order rank of the
 // thread's first escape in each group, and the escape masks.
 struct TileEsc {
-  uint32_t agg;             // escapes in the tile
-  uint32_t lds_groups = 0;  // BF16 dense encode: groups whose exponents went to LDS (bit g; same in a wave)
-  uint32_t rank[4];         // per group (4 groups: BF16 8 elements per thread, E5M2 16)
-  uint32_t mask[4];         // escaped elements of each group, bit j = element j
+  uint32_t agg;      // escapes in the tile
+  uint32_t rank[4];  // per group (4 groups: BF16 8 elements per thread, E5M2 16)
+  uint32_t mask[4];  // escaped elements of each group, bit j = element j
 };
 
 __device__ inline void wave_totals_to_lds(EncShared& sh, uint32_t i01, uint32_t i23, uint32_t tid) {
@@ -423,7 +423,10 @@ __device__ inline TileIn load_tile_bf16(const EncArgs& a, uint64_t tile, uint32_
   uint4* w = in.w;
   if (first + kEncTileBf16 <= a.n) {  // same in every thread
 #pragma unroll
-    for (int g = 0; g < 4; ++g) w[g] = *reinterpret_cast<const uint4*>(src + g * 2048 + 8 * tid);
+    for (int g = 0; g < 4; ++g) {  // read once: non-temporal
+      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + g * 2048 + 8 * tid));
+      w[g] = make_uint4(v.x, v.y, v.z, v.w);
+    }
     return in;
   }
 #pragma unroll
@@ -459,13 +462,12 @@ __device__ inline uint32_t codes12(uint32_t w) {
   return (v & 0x3Fu) | ((v >> 10) & 0xFC0u);
 }
 
-// With `exps` (the dense kernel), a group in which at least kLdsLanes of a
-// wave's threads hold escapes has every thread's 8 exponent bytes written to
-// exps[element] and its bit set in lds_groups: the escape pass then reads
-// them from LDS instead of reading the input again.  Few escapes (the common
-// case) skip the writes; many escapes would otherwise cost each wave one
-// dependent global load per escape of a thread.
-constexpr uint32_t kLdsLanes = 4;
+// With `exps` (the dense kernel), every thread of a wave in which any thread
+// holds an escape in a group writes that group's 8 exponent bytes to
+// exps[element]: the escape pass reads them there, so the input is read
+// once, with non-temporal loads (re-reading an escape's exponent from the
+// input would then miss the cache).  Groups without escapes in the wave skip
+// the writes.
 
 template <int kVariant = kMain>
 __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store,
@@ -493,8 +495,7 @@ __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t ti
     const uint32_t f = ((lo >> 4) & 0x01010101u) | ((hi >> 3) & 0x02020202u);
     r.mask[g] = f;
     cnt[g] = __builtin_popcount(f);
-    if (exps && __popcll(__ballot(f != 0)) >= kLdsLanes) {  // same in the wave
-      r.lds_groups |= 1u << g;
+    if (exps && __ballot(f != 0)) {  // same in the wave
       const uint32_t e03 = perm((x.y >> 7) & 0x00FF00FFu, (x.x >> 7) & 0x00FF00FFu, 0x06040200u);
       const uint32_t e47 = perm((x.w >> 7) & 0x00FF00FFu, (x.z >> 7) & 0x00FF00FFu, 0x06040200u);
       *reinterpret_cast<uint2*>(exps + local) = make_uint2(e03, e47);
@@ -547,45 +548,23 @@ __device__ TileEsc encode_tile_bf16(const EncArgs& a, EncShared& sh, uint64_t ti
 
 // The escapes of one BF16 tile: position in chunk and raw exponent, handed
 // to `put(rank, pos, exponent)` in element order (a thread's escapes of one
-// group have consecutive ranks).
-//
-// Dense kernel: the exponents of LDS groups (lds_groups) come from `exps`;
-// the others are read again from the input, the first escape of each of the
-// four groups with loads issued together (keeping the input registers live
-// through the rank scan instead measured slower).
+// group have consecutive ranks).  Dense kernel: the exponents come from
+// `exps` (every group with an escape in the thread's wave was written there).
 template <typename Put>
-__device__ inline void dense_escapes_bf16(const EncArgs& a, uint64_t tile, const TileEsc& r, const uint8_t* exps,
-                                          Put put) {
+__device__ inline void dense_escapes_bf16(uint64_t tile, const TileEsc& r, const uint8_t* exps, Put put) {
   const uint32_t tid = threadIdx.x;
-  const uint16_t* in16 = reinterpret_cast<const uint16_t*>(a.in) + tile * kEncTileBf16;
   const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTileBf16;
-  uint32_t m[4], x0[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const uint32_t f = r.mask[g];  // element k at bit 8k, element 4 + k at bit 8k + 1
-    m[g] = f ? flag_mask4(f << 4) | (flag_mask4(f << 3) << 4) : 0u;  // element order
-    if (m[g] && !((r.lds_groups >> g) & 1)) x0[g] = in16[g * 2048 + 8 * tid + __builtin_ctz(m[g])];
-  }
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    uint32_t mg = m[g], k = r.rank[g];
-    if (!mg) continue;
+    if (!f) continue;
+    uint32_t m = flag_mask4(f << 4) | (flag_mask4(f << 3) << 4), k = r.rank[g];  // element order
     const uint32_t local = g * 2048 + 8 * tid;
-    if ((r.lds_groups >> g) & 1) {  // same in the wave
-      const uint2 e = *reinterpret_cast<const uint2*>(exps + local);
-      while (mg) {
-        const uint32_t j = __builtin_ctz(mg);
-        mg &= mg - 1;
-        put(k++, in_chunk + local + j, ((j < 4 ? e.x : e.y) >> (8 * (j & 3))) & 0xFF);
-      }
-    } else {
-      uint32_t x = x0[g];
-      while (mg) {
-        const uint32_t j = __builtin_ctz(mg);
-        mg &= mg - 1;
-        put(k++, in_chunk + local + j, (x >> 7) & 0xFF);
-        if (mg) x = in16[local + __builtin_ctz(mg)];
-      }
+    const uint2 e = *reinterpret_cast<const uint2*>(exps + local);
+    while (m) {
+      const uint32_t j = __builtin_ctz(m);
+      m &= m - 1;
+      put(k++, in_chunk + local + j, ((j < 4 ? e.x : e.y) >> (8 * (j & 3))) & 0xFF);
     }
   }
 }
@@ -706,8 +685,10 @@ __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t ti
   return r;
 }
 
-// The escapes of one E5M2 tile, as dense_escapes_bf16 / window_escapes_bf16
-// (the dense kernel reads every exponent again from the input).
+// The escapes of one E5M2 tile, handed to `put` as for BF16.  Dense kernel:
+// each exponent is read again from the input (an LDS copy of a tile's 16,384
+// exponents would cost occupancy), the first escape of each of the four
+// groups with loads issued together.
 template <typename Put>
 __device__ inline void dense_escapes_e5m2(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put) {
   const uint32_t tid = threadIdx.x;
@@ -783,7 +764,7 @@ __device__ inline void put_record_group(const EncArgs& a, uint64_t idx, uint32_t
 template <bool kBf16, int kVariant = kMain>
 __device__ void encode_dense(const EncArgs& a) {
   __shared__ EncShared sh;
-  __shared__ alignas(8) uint8_t exps[kBf16 ? kEncTileBf16 : 8];  // BF16: exponents of LDS groups, by element
+  __shared__ alignas(8) uint8_t exps[kBf16 ? kEncTileBf16 : 8];  // BF16: exponent bytes, by element
   const uint64_t t = blockIdx.x;
   const TileIn in = kBf16 ? load_tile_bf16(a, t) : load_tile_e5m2(a, t);  // in flight during the table build
   build_table<kVariant>(a, sh, a.seg_chunks ? codebook_of_chunk(t >> (kBf16 ? 3 : 2), a.seg_chunks) : 0,
@@ -798,7 +779,7 @@ __device__ void encode_dense(const EncArgs& a) {
     // stores instead of scattered 4-byte ones
     uint32_t* rec = sh.pos4;
     auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) { rec[k] = pos | (val << 16); };
-    if (kBf16) dense_escapes_bf16(a, t, r, exps, stage);
+    if (kBf16) dense_escapes_bf16(t, r, exps, stage);
     else dense_escapes_e5m2(a, t, r, stage);
     __syncthreads();
     uint32_t* slot = a.stage + t * kSlot;
