@@ -9,6 +9,9 @@ ROOT = os.path.dirname(HERE)
 SRCS = [os.path.join(HERE, "csrc", "splitzip.hip"), os.path.join(HERE, "csrc", "pipeline.hip"),
         os.path.join(HERE, "csrc", "calibrate.hip")]
 LIB = os.path.join(HERE, "libsplitzip.so")
+# the benchmark's copy / read ceiling kernels, a library of their own
+CEILING_SRC = os.path.join(HERE, "csrc", "copy_ceiling.hip")
+CEILING_LIB = os.path.join(HERE, "libszceiling.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -23,13 +26,18 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *SRCS]
+def _compile(srcs, lib, verbose):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(SRCS, LIB, verbose)
+    _compile([CEILING_SRC], CEILING_LIB, verbose)
     return LIB
 
 
