@@ -18,11 +18,12 @@
 //                 16-byte loads issued before the codebook tables are built
 //                 in LDS, then codes, nibbles and sign|mantissa bytes with
 //                 byte permutes (E5M2: one OR of four per-byte-position
-//                 table words per input word), non-temporal lane-contiguous
+//                 exponent-table words per input word, the sign|mantissa
+//                 triples by shifts and masks), non-temporal lane-contiguous
 //                 stores, element-order escape ranks (wave64 DPP scan +
 //                 LDS), escape records staged per tile in the workspace
-//                 (BF16: input read once with non-temporal loads, the
-//                 exponents of groups with escapes kept in LDS).
+//                 (input read once with non-temporal loads; the exponents
+//                 of groups with escapes kept in LDS).
 //   encode_sums   escape count of each block of 64 tiles.
 //   encode_place  per range of 8 to 64 tiles: base (lower super-blocks,
 //                 blocks and tiles), tile scan, chunk offsets, staged records
@@ -298,9 +299,11 @@ constexpr uint32_t kBlockTiles = 64;  // tiles per block of the escape-count sum
 
 struct EncShared {
   uint8_t table[256];
-  // E5M2: word for input byte b at byte position j of a 4-element word:
-  // code << 4j | (sign << 2 | mantissa) << (16 + 3j) | escaped << (28 + j).
-  // After the tile's rank scan it holds the tile's staged escape records.
+  // E5M2: words 32j + e, for the exponent e of the element at byte position
+  // j of a 4-element word: code << 4j | escaped << (28 + j).  Indexed by the
+  // 5-bit exponent, lanes holding the same exponent read one address
+  // (broadcast) and different exponents fall in different banks.  After the
+  // tile's rank scan the array holds the tile's staged escape records.
   uint32_t pos4[4 * 256];
   uint32_t wave[8];
   uint64_t red[16];
@@ -310,15 +313,9 @@ struct EncShared {
 static_assert(stage_slot(kMain) <= 4 * 256 && stage_slot(kTop8) <= 4 * 256,
               "staged records reuse the E5M2 table space");
 
-constexpr uint32_t kPlaceRecs = 2048;  // escape records per LDS window of encode_place
+constexpr uint32_t kPlaceRecs = 2048;  // escape records per LDS window of place_range
 constexpr uint32_t kPlaceWgs = 2048;   // encode_place aims at this many workgroups
 
-struct PlaceShared {
-  uint64_t red[16];
-  uint32_t pre_all[kBlockTiles + 1];     // escapes before each tile of the range
-  uint32_t pre_staged[kBlockTiles + 1];  // staged records before each tile of the range
-  alignas(16) uint32_t rec[kPlaceRecs];  // re-encoded tile's records (position | exponent << 16) in escape order
-};
 
 // Exclusive prefix over the workgroup's threads (thread order) of per-thread
 // u32 values whose sum over the workgroup fits 32 bits; *total gets the sum.
@@ -352,12 +349,10 @@ __device__ inline void build_table(const EncArgs& a, EncShared& sh, uint64_t cbi
   if (tid < kCodes) sh.table[a.cb_args ? a.prep.cbs[16 * cbi + tid] : a.out[64 + 16 * cbi + tid]] = (uint8_t)tid;
   __syncthreads();
   if (entries == 32) {  // E5M2 per-position words, from the exponent table
-    const uint32_t b = tid & 0xFFu;
-    const uint32_t c = sh.table[(b >> 2) & 0x1Fu];
-    const uint32_t code = c & 0xFu, esc = c >> 4;  // kEsc: code 0, escaped
-    const uint32_t tri = ((b >> 5) & 4u) | (b & 3u);
-#pragma unroll
-    for (uint32_t j = 0; j < 4; ++j) sh.pos4[256 * j + b] = (code << (4 * j)) | (tri << (16 + 3 * j)) | (esc << (28 + j));
+    if (tid < 128) {
+      const uint32_t j = tid >> 5, c = sh.table[tid & 31u];
+      sh.pos4[tid] = ((c & 0xFu) << (4 * j)) | ((c >> 4) << (28 + j));  // kEsc: code 0, escaped
+    }
     __syncthreads();
   }
 }
@@ -604,7 +599,10 @@ __device__ inline TileIn load_tile_e5m2(const EncArgs& a, uint64_t tile, uint32_
   const uint8_t* src = a.in + first;
   if (first + kEncTileE5m2 <= a.n) {  // same in every thread
 #pragma unroll
-    for (int g = 0; g < 4; ++g) in.w[g] = *reinterpret_cast<const uint4*>(src + g * 4096 + 16 * tid);
+    for (int g = 0; g < 4; ++g) {
+      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + g * 4096 + 16 * tid));
+      in.w[g] = make_uint4(v.x, v.y, v.z, v.w);
+    }
     return in;
   }
 #pragma unroll
@@ -620,15 +618,31 @@ __device__ inline TileIn load_tile_e5m2(const EncArgs& a, uint64_t tile, uint32_
   return in;
 }
 
-// Per-position table words of the four bytes of x, OR-ed: nibble codes of
-// the four elements in bits 0..15, their triples in bits 16..27, escape
-// flags in bits 28..31.
+// Per-position table words of the exponents of the four bytes of x, OR-ed:
+// nibble codes of the four elements in bits 0..15, escape flags in bits
+// 28..31.
 __device__ inline uint32_t e5m2_pos_word(const uint32_t* pos4, uint32_t x) {
-  return pos4[x & 0xFFu] | pos4[256 + ((x >> 8) & 0xFFu)] | pos4[512 + ((x >> 16) & 0xFFu)] | pos4[768 + (x >> 24)];
+  return pos4[(x >> 2) & 0x1Fu] | pos4[32 + ((x >> 10) & 0x1Fu)] | pos4[64 + ((x >> 18) & 0x1Fu)] |
+         pos4[96 + ((x >> 26) & 0x1Fu)];
+}
+
+// Sign|mantissa triples (sign << 2 | mantissa) of the four bytes of x, the
+// element at byte j in bits 3j..3j+2: the triples land in bytes, then pairs
+// of bytes are merged and the two halves joined.
+__device__ inline uint32_t e5m2_tri12(uint32_t x) {
+  const uint32_t t = ((x >> 5) & 0x04040404u) | (x & 0x03030303u);
+  const uint32_t v = t | (t >> 5);  // bits 0..5: t0 | t1 << 3; bits 16..21: t2 | t3 << 3
+  return (v & 0x3Fu) | ((v >> 10) & 0xFC0u);
+}
+
+constexpr uint32_t kEscSlots = 16;  // per wave and group: input words of lanes with escapes kept in LDS
+
+__device__ inline uint32_t lane_slot(uint64_t bal) {  // lanes below this one in bal
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }
 
 __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t tile, const TileIn& in, bool store,
-                                   uint32_t tid = threadIdx.x) {
+                                   uint32_t tid = threadIdx.x, uint4* escw = nullptr) {
   const uint32_t lane = tid & 63, wave = tid >> 6;
   const uint64_t first = tile * kEncTileE5m2;
   const bool tile_full = first + kEncTileE5m2 <= a.n;  // same in every thread
@@ -642,8 +656,9 @@ __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t ti
     // escape flags in element order, nibbles, 16 triples = 48 bits (element i at bit 3i)
     uint32_t f = (r0 >> 28) | ((r1 >> 24) & 0xF0u) | ((r2 >> 20) & 0xF00u) | ((r3 >> 16) & 0xF000u);
     uint2 nib = make_uint2(perm(r1, r0, 0x05040100u), perm(r3, r2, 0x05040100u));
-    uint32_t lo = ((r0 >> 16) & 0xFFFu) | ((r1 >> 4) & 0xFFF000u) | ((r2 << 8) & 0xFF000000u);
-    uint32_t hi = ((r2 >> 24) & 0xFu) | ((r3 >> 12) & 0xFFF0u);
+    const uint32_t t2 = e5m2_tri12(in.w[g].z);
+    uint32_t lo = e5m2_tri12(in.w[g].x) | (e5m2_tri12(in.w[g].y) << 12) | (t2 << 24);
+    uint32_t hi = (t2 >> 8) | (e5m2_tri12(in.w[g].w) << 4);
     uint32_t valid = 16;
     if (!tile_full) {  // elements past n: no code, no triple, no escape
       valid = valid_in_group(a.n, first + local, 16);
@@ -656,6 +671,13 @@ __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t ti
     }
     r.mask[g] = f;
     cnt[g] = __builtin_popcount(f);
+    if (escw) {
+      const uint64_t bal = __ballot(f != 0);
+      if (bal) {  // same in the wave
+        const uint32_t slot = lane_slot(bal);
+        if (f && slot < kEscSlots) escw[(wave * 4 + g) * kEscSlots + slot] = in.w[g];
+      }
+    }
     if (!store) continue;
     if (tile_full) {
       store_stream(a.out + a.nib + (first + local) / 2, nib);
@@ -686,27 +708,37 @@ __device__ TileEsc encode_tile_e5m2(const EncArgs& a, EncShared& sh, uint64_t ti
 }
 
 // The escapes of one E5M2 tile, handed to `put` as for BF16.  Dense kernel:
-// each exponent is read again from the input (an LDS copy of a tile's 16,384
-// exponents would cost occupancy), the first escape of each of the four
-// groups with loads issued together.
+// the input is read once (non-temporal loads); during the encode pass each
+// lane holding escapes in a group stored its 16-byte input word in its wave's
+// LDS slots for that group (the lane's rank among such lanes), so the
+// exponents come from LDS; a lane ranked beyond the kEscSlots slots (more
+// than 16 lanes of a wave with escapes in one group) reads its word again
+// from the input.
 template <typename Put>
-__device__ inline void dense_escapes_e5m2(const EncArgs& a, uint64_t tile, const TileEsc& r, Put put) {
-  const uint32_t tid = threadIdx.x;
+__device__ inline void dense_escapes_e5m2(const EncArgs& a, uint64_t tile, const TileEsc& r, const uint4* escw,
+                                          Put put) {
+  const uint32_t tid = threadIdx.x, wave = tid >> 6;
   const uint8_t* in8 = a.in + tile * kEncTileE5m2;
   const uint32_t in_chunk = (uint32_t)(tile & 3) * (uint32_t)kEncTileE5m2;
-  uint32_t x0[4] = {0, 0, 0, 0};
+  uint32_t slot[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
-    if (r.mask[g]) x0[g] = in8[g * 4096 + 16 * tid + __builtin_ctz(r.mask[g])];
+  for (int g = 0; g < 4; ++g) slot[g] = lane_slot(__ballot(r.mask[g] != 0));
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    uint32_t m = r.mask[g], k = r.rank[g], x = x0[g];
+    uint32_t m = r.mask[g], k = r.rank[g];
+    if (!m) continue;
     const uint32_t local = g * 4096 + 16 * tid;
+    uint4 w;
+    if (slot[g] < kEscSlots) {
+      w = escw[(wave * 4 + g) * kEscSlots + slot[g]];
+    } else {  // more lanes with escapes than slots: the input again
+      w = *reinterpret_cast<const uint4*>(in8 + local);
+    }
     while (m) {
       const uint32_t j = __builtin_ctz(m);
       m &= m - 1;
+      const uint32_t x = pick4(w.x, w.y, w.z, w.w, j >> 2) >> (8 * (j & 3));
       put(k++, in_chunk + local + j, (x >> 2) & 0x1F);
-      if (m) x = in8[local + __builtin_ctz(m)];
     }
   }
 }
@@ -761,16 +793,24 @@ __device__ inline void put_record_group(const EncArgs& a, uint64_t idx, uint32_t
   d[2] = ((r2 >> 16) & 0xFFu) | (r3 << 8);
 }
 
+// LDS of a dense tile encode beside EncShared: BF16, the exponent bytes by
+// element; E5M2, the input words of lanes with escapes.
+template <bool kBf16>
+struct DenseLds {
+  alignas(16) uint8_t exps[kBf16 ? kEncTileBf16 : 16 * 16 * kEscSlots];
+};
+
+// Tile t: dense encode, its escape count to the workspace and, when they fit
+// its slot, its escape records staged there.
 template <bool kBf16, int kVariant = kMain>
-__device__ void encode_dense(const EncArgs& a) {
-  __shared__ EncShared sh;
-  __shared__ alignas(8) uint8_t exps[kBf16 ? kEncTileBf16 : 8];  // BF16: exponent bytes, by element
-  const uint64_t t = blockIdx.x;
+__device__ void dense_tile(const EncArgs& a, EncShared& sh, DenseLds<kBf16>& dl, uint64_t t) {
+  uint8_t* exps = dl.exps;
   const TileIn in = kBf16 ? load_tile_bf16(a, t) : load_tile_e5m2(a, t);  // in flight during the table build
   build_table<kVariant>(a, sh, a.seg_chunks ? codebook_of_chunk(t >> (kBf16 ? 3 : 2), a.seg_chunks) : 0,
                         kBf16 ? 256u : 32u);
-  const TileEsc r =
-      kBf16 ? encode_tile_bf16<kVariant>(a, sh, t, in, true, threadIdx.x, exps) : encode_tile_e5m2(a, sh, t, in, true);
+  uint4* escw = reinterpret_cast<uint4*>(exps);
+  const TileEsc r = kBf16 ? encode_tile_bf16<kVariant>(a, sh, t, in, true, threadIdx.x, exps)
+                          : encode_tile_e5m2(a, sh, t, in, true, threadIdx.x, escw);
   if (threadIdx.x == 0) a.tile_count[t] = r.agg;
   constexpr uint32_t kSlot = stage_slot(kVariant);
   if (r.agg <= kSlot) {  // uniform
@@ -780,11 +820,18 @@ __device__ void encode_dense(const EncArgs& a) {
     uint32_t* rec = sh.pos4;
     auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) { rec[k] = pos | (val << 16); };
     if (kBf16) dense_escapes_bf16(t, r, exps, stage);
-    else dense_escapes_e5m2(a, t, r, stage);
+    else dense_escapes_e5m2(a, t, r, escw, stage);
     __syncthreads();
     uint32_t* slot = a.stage + t * kSlot;
     for (uint32_t i = threadIdx.x; i < r.agg; i += kThreads) slot[i] = rec[i];
   }
+}
+
+template <bool kBf16, int kVariant = kMain>
+__device__ void encode_dense(const EncArgs& a) {
+  __shared__ EncShared sh;
+  __shared__ DenseLds<kBf16> dl;
+  dense_tile<kBf16, kVariant>(a, sh, dl, blockIdx.x);
 }
 
 __global__ __launch_bounds__(kThreads) void encode_dense_bf16_kernel(EncArgs a) { encode_dense<true>(a); }
@@ -846,73 +893,65 @@ __device__ void write_records(const EncArgs& a, const uint32_t* rec, uint64_t d0
   }
 }
 
-// One workgroup per range of place_tiles tiles (a power of two up to
-// kBlockTiles, so a range lies inside one block): the range's base (escapes
-// of the lower super-blocks, of the lower blocks of its super-block and of
-// the lower tiles of its block), the scan of its tiles' counts, its chunk
-// offsets (E, S and the stream size for the last range), its staged records
-// moved to their place, and its tiles whose escapes overflowed their slot
+// LDS of place_range for ranges of up to kMax tiles.
+template <uint32_t kMax>
+struct PlaceLds {
+  uint64_t red[16];
+  uint32_t pre_all[kMax + 1];     // escapes before each tile of the range
+  uint32_t pre_staged[kMax + 1];  // staged records before each tile of the range
+  alignas(16) uint32_t rec[kPlaceRecs];  // re-encoded tile's records (position | exponent << 16) in escape order
+};
+
+// The tiles [t0, t0 + tiles) (tiles <= kMax <= 4 * kThreads), whose first
+// escape has stream index `base`: the scan of
+// their counts (kMax / kThreads consecutive tiles per thread, so the thread
+// order is the tile order), their chunk offsets (E, S and the stream size
+// when the last tile of the stream is among them), their staged records
+// moved to their place, and the tiles whose escapes overflowed their slot
 // encoded again.
-template <bool kBf16, int kVariant = kMain>
-__device__ void encode_place(const EncArgs& a) {
+template <bool kBf16, int kVariant, uint32_t kMax>
+__device__ void place_range(const EncArgs& a, PlaceLds<kMax>& sh, EncShared& esh, uint64_t t0, uint32_t tiles,
+                            uint64_t base) {
   constexpr uint64_t kRec = kVariant == kSentinel ? 1 : 3;  // stream bytes per escape
-  __shared__ PlaceShared sh;
-  __shared__ EncShared esh;
-  if (a.prep_in == 2 && blockIdx.x == gridDim.x - 1) {  // the launch's extra workgroup
-    prep_work(a.prep, 0, 1);
-    return;
-  }
-  const uint32_t tid = threadIdx.x;
-  const uint64_t t0 = (uint64_t)blockIdx.x * a.place_tiles;
-  const uint32_t tiles = (uint32_t)std::min<uint64_t>(a.place_tiles, a.n_tiles - t0);
-  const uint64_t blk = t0 / kBlockTiles;
-  const uint32_t below = (uint32_t)(t0 % kBlockTiles);  // tiles of the block before the range
-  const uint64_t t = t0 + tid;
-  const bool mine = tid < tiles;
-  const uint32_t cnt = mine ? a.tile_count[t] : 0u;
+  constexpr uint32_t kPer = (kMax + kThreads - 1) / kThreads;  // tiles per thread
   constexpr uint32_t kSlot = stage_slot(kVariant);
-  const bool over = cnt > kSlot;
-
-  // base: the first wave adds the lower blocks of the super-block, the
-  // second the lower tiles of the block, all waves the lower super-blocks;
-  // with at most 64 blocks (no block sums) all waves add the lower tiles
-  uint64_t lower = 0;
-  if (a.sums_in_place) {
-    for (uint32_t i = tid; i < (uint32_t)t0; i += kThreads) lower += a.tile_count[i];
-  } else {
-    for (uint64_t i = tid; i < (blk >> 6); i += kThreads) lower += a.super_sum[i];
-    if (tid < (blk & 63)) lower += a.block_sum[(blk & ~63ull) + tid];
-    if (tid >= 64 && tid - 64 < below) lower += a.tile_count[blk * kBlockTiles + (tid - 64)];
-  }
-  {
-    // wave sum of u64 through two u32 halves; one lane per wave stores it
-    uint64_t v = lower;
+  const uint32_t tid = threadIdx.x;
+  uint32_t cnt[kPer], sum = 0, ssum = 0;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
-      const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
-      v += ((uint64_t)hi << 32) | lo;
-    }
-    if ((tid & 63) == 0) sh.red[8 + (tid >> 6)] = v;
+  for (uint32_t k = 0; k < kPer; ++k) {
+    const uint32_t i = tid * kPer + k;
+    cnt[k] = i < tiles ? a.tile_count[t0 + i] : 0u;
+    sum += cnt[k];
+    ssum += cnt[k] > kSlot ? 0u : cnt[k];
   }
-  __syncthreads();
-  const uint64_t base = sh.red[8] + sh.red[9] + sh.red[10] + sh.red[11];
-
-  // in-range offsets of the tiles
   uint32_t total, staged_total;
-  const uint32_t pre = block_exclusive_sum<kThreads / 64>(sh.red, cnt, &total);
-  const uint32_t spre = block_exclusive_sum<kThreads / 64>(sh.red, over ? 0u : cnt, &staged_total);
-  if (tid <= kBlockTiles) {
-    sh.pre_all[tid] = pre;
-    sh.pre_staged[tid] = spre;
+  uint32_t pre = block_exclusive_sum<kThreads / 64>(sh.red, sum, &total);
+  uint32_t spre = block_exclusive_sum<kThreads / 64>(sh.red, ssum, &staged_total);
+#pragma unroll
+  for (uint32_t k = 0; k < kPer; ++k) {
+    const uint32_t i = tid * kPer + k;
+    if (i <= kMax) {
+      sh.pre_all[i] = pre;
+      sh.pre_staged[i] = spre;
+    }
+    pre += cnt[k];
+    spre += cnt[k] > kSlot ? 0u : cnt[k];
+  }
+  if (tid == 0 && kPer * kThreads <= kMax) {  // entry kMax, past every thread's tiles
+    sh.pre_all[kMax] = total;
+    sh.pre_staged[kMax] = staged_total;
   }
   const bool any_over = staged_total != total;  // uniform
   __syncthreads();
-  if (mine) {
-    constexpr uint32_t kTpcLog2 = kBf16 ? 3 : 2;  // tiles per chunk: 8 BF16, 4 E5M2
-    if ((t & ((1u << kTpcLog2) - 1)) == 0) put_le(a.out + a.offsets + 8 * (t >> kTpcLog2), base + pre, 8);
+  constexpr uint32_t kTpcLog2 = kBf16 ? 3 : 2;  // tiles per chunk: 8 BF16, 4 E5M2
+#pragma unroll
+  for (uint32_t k = 0; k < kPer; ++k) {
+    const uint32_t i = tid * kPer + k;
+    if (i >= tiles) continue;
+    const uint64_t t = t0 + i;
+    if ((t & ((1u << kTpcLog2) - 1)) == 0) put_le(a.out + a.offsets + 8 * (t >> kTpcLog2), base + sh.pre_all[i], 8);
     if (t == a.n_tiles - 1) {
-      const uint64_t e = std::min<uint64_t>(base + pre + cnt, a.n);
+      const uint64_t e = std::min<uint64_t>(base + sh.pre_all[i] + cnt[k], a.n);
       const uint64_t s = a.esc + kRec * e;
       put_le(a.out + a.offsets + 8 * a.chunks, e, 8);
       put_le(a.out + 16, e, 8);
@@ -951,7 +990,7 @@ __device__ void encode_place(const EncArgs& a) {
       uint32_t v[4];
 #pragma unroll
       for (uint32_t k = 0; k < 4; ++k) {
-        while (i + 1 < tiles && sh.pre_staged[i + 1] <= j + k) ++i;  // at most a few steps: tiles hold records
+        if (i + 1 < tiles && sh.pre_staged[i + 1] <= j + k) i = tile_of(j + k);  // record j + k is in a later tile
         v[k] = a.stage[(t0 + i) * kSlot + (j + k - sh.pre_staged[i])];
       }
       put_record_group<kVariant>(a, base + j, v[0], v[1], v[2], v[3]);
@@ -1011,10 +1050,56 @@ __device__ void encode_place(const EncArgs& a) {
   }
 }
 
+// One workgroup per range of place_tiles tiles (a power of two up to
+// kBlockTiles, so a range lies inside one block): the range's base (escapes
+// of the lower super-blocks, of the lower blocks of its super-block and of
+// the lower tiles of its block), then place_range.
+template <bool kBf16, int kVariant = kMain>
+__device__ void encode_place(const EncArgs& a) {
+  __shared__ PlaceLds<kBlockTiles> sh;
+  __shared__ EncShared esh;
+  if (a.prep_in == 2 && blockIdx.x == gridDim.x - 1) {  // the launch's extra workgroup
+    prep_work(a.prep, 0, 1);
+    return;
+  }
+  const uint32_t tid = threadIdx.x;
+  const uint64_t t0 = (uint64_t)blockIdx.x * a.place_tiles;
+  const uint32_t tiles = (uint32_t)std::min<uint64_t>(a.place_tiles, a.n_tiles - t0);
+  const uint64_t blk = t0 / kBlockTiles;
+  const uint32_t below = (uint32_t)(t0 % kBlockTiles);  // tiles of the block before the range
+
+  // base: the first wave adds the lower blocks of the super-block, the
+  // second the lower tiles of the block, all waves the lower super-blocks;
+  // with at most 64 blocks (no block sums) all waves add the lower tiles
+  uint64_t lower = 0;
+  if (a.sums_in_place) {
+    for (uint32_t i = tid; i < (uint32_t)t0; i += kThreads) lower += a.tile_count[i];
+  } else {
+    for (uint64_t i = tid; i < (blk >> 6); i += kThreads) lower += a.super_sum[i];
+    if (tid < (blk & 63)) lower += a.block_sum[(blk & ~63ull) + tid];
+    if (tid >= 64 && tid - 64 < below) lower += a.tile_count[blk * kBlockTiles + (tid - 64)];
+  }
+  {
+    // wave sum of u64 through two u32 halves; one lane per wave stores it
+    uint64_t v = lower;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
+      const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
+      v += ((uint64_t)hi << 32) | lo;
+    }
+    if ((tid & 63) == 0) sh.red[8 + (tid >> 6)] = v;
+  }
+  __syncthreads();
+  const uint64_t base = sh.red[8] + sh.red[9] + sh.red[10] + sh.red[11];
+  place_range<kBf16, kVariant, kBlockTiles>(a, sh, esh, t0, tiles, base);
+}
+
 __global__ __launch_bounds__(kThreads) void encode_place_bf16_kernel(EncArgs a) { encode_place<true>(a); }
 __global__ __launch_bounds__(kThreads) void encode_place_e5m2_kernel(EncArgs a) { encode_place<false>(a); }
 __global__ __launch_bounds__(kThreads) void encode_place_sentinel_kernel(EncArgs a) { encode_place<true, kSentinel>(a); }
 __global__ __launch_bounds__(kThreads) void encode_place_top8_kernel(EncArgs a) { encode_place<true, kTop8>(a); }
+
 
 // ---------------------------------------------------------- decode kernels
 struct DecArgs {
@@ -1064,6 +1149,37 @@ __device__ bool read_header(const DecArgs& a, Header& h) {
 
 __device__ inline void report_corrupt(int32_t* status) {
   if (status) __hip_atomic_store(status, (int32_t)SPLITZIP_E_CORRUPT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whether v equals the value of another lane of its 16-lane row: the 15
+// row rotations (DPP row_ror 1..15) of v, compared with v.
+template <int kRot = 1>
+__device__ inline bool row_has_duplicate(uint32_t v) {
+  if constexpr (kRot == 16) {
+    return false;
+  } else {
+    const bool same = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + kRot, 0xf, 0xf, false) == v;
+    return same | row_has_duplicate<kRot + 1>(v);
+  }
+}
+
+// Every codebook of the stream must hold 16 distinct entries, each below
+// vmax (32 for E5M2; any byte for BF16), as a stream the encoder writes
+// does.  The K codebooks are spread over the launch's workgroups, four per
+// pass of one full wave: lane l holds entry l & 15 of codebook 4q + (l >> 4)
+// and compares it with the 15 other entries of its 16-lane row through DPP
+// row rotations.  Reports a bad stream through the status word.
+__device__ inline void check_codebooks(const DecArgs& a, uint64_t k, uint32_t vmax) {
+  const uint32_t lane = __lane_id();
+  bool bad = false;
+  const uint32_t quads = (uint32_t)(k + 3) / 4;  // k <= 65535 (header check)
+  for (uint32_t q = blockIdx.x; q < quads; q += gridDim.x) {  // same in the wave
+    const uint32_t cb = 4 * q + (lane >> 4);
+    const bool live = cb < k;  // same in each 16-lane row
+    const uint32_t v = live ? a.in[64 + 16 * cb + (lane & 15)] : 0u;
+    bad |= live && (row_has_duplicate(v) || v >= vmax);
+  }
+  if (__ballot(bad) != 0 && lane == 0) report_corrupt(a.status);
 }
 
 __device__ inline uint32_t record_pos(const uint8_t* rec) { return rec[0] | ((uint32_t)rec[1] << 8); }
@@ -1188,7 +1304,9 @@ __device__ bool stage_escapes(const DecArgs& a, const Header& h, uint64_t tile, 
   const uint32_t win_len = (uint32_t)std::min<uint64_t>(kDecTile, chunk_len - win_lo);
   const bool last_in_chunk = win_lo + win_len == chunk_len;
   const uint64_t lo = f.lo, hi = f.hi;
-  bool ok = lo <= hi && hi <= h.e;
+  // at most one record per element of the chunk (this also bounds the
+  // record ranges kept as 32-bit counts below)
+  bool ok = lo <= hi && hi <= h.e && hi - lo <= chunk_len;
   if (chunk == 0 && lo != 0) ok = false;
   if (chunk == h.chunks - 1 && hi != h.e) ok = false;
   if (!ok) return false;  // uniform: every thread read the same words
@@ -1317,6 +1435,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
   }
   if (a.n == 0) {  // header-only stream: off[0] must be 0
     if (threadIdx.x == 0 && ld64(a.in + h.s.offsets) != 0) report_corrupt(a.status);
+    if (threadIdx.x < 64) check_codebooks(a, h.k, a.dtype == SPLITZIP_BF16 ? 256u : 32u);
     return;
   }
   const uint64_t tile = blockIdx.x;
@@ -1360,6 +1479,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
       if (esc8) bf16_patch8(o, esc8, *reinterpret_cast<const uint2*>(vals + local));
       store_stream(out_t + 2 * local, o);
     }
+    if (tid < 64) check_codebooks(a, h.k, 256u);
     return;
   }
   // last tile: byte-wise loads and stores
@@ -1382,6 +1502,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecArgs a) {
     if (esc8) bf16_patch8(o, esc8, *reinterpret_cast<const uint2*>(vals + local));
     for (uint32_t j = 0; j < valid; ++j) out16[e0 + j] = (uint16_t)(pick4(o.x, o.y, o.z, o.w, j >> 1) >> (16 * (j & 1)));
   }
+  if (tid < 64) check_codebooks(a, h.k, 256u);
 }
 
 // E5M2 decode of 16 elements: the 16 codes (8 nibble bytes) through the
@@ -1443,6 +1564,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
   }
   if (a.n == 0) {  // header-only stream: off[0] must be 0
     if (threadIdx.x == 0 && ld64(a.in + h.s.offsets) != 0) report_corrupt(a.status);
+    if (threadIdx.x < 64) check_codebooks(a, h.k, a.dtype == SPLITZIP_BF16 ? 256u : 32u);
     return;
   }
   const uint64_t tile = blockIdx.x;
@@ -1492,6 +1614,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
       if (esc16) e5m2_patch16(o, esc16, *reinterpret_cast<const uint4*>(vals + local));
       store_stream(out_t + local, o);
     }
+    if (tid < 64) check_codebooks(a, h.k, 32u);
     return;
   }
   // last tile: byte-wise loads and stores
@@ -1515,6 +1638,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(DecArgs a) {
     if (esc16) e5m2_patch16(o, esc16, *reinterpret_cast<const uint4*>(vals + local));
     for (uint32_t j = 0; j < valid; ++j) a.out[e0 + j] = (uint8_t)(pick4(o.x, o.y, o.z, o.w, j >> 2) >> (8 * (j & 3)));
   }
+  if (tid < 64) check_codebooks(a, h.k, 32u);
 }
 
 // ---------------------------------------------- ablation decoders (BF16)
@@ -1551,6 +1675,7 @@ __global__ __launch_bounds__(kThreads) void decode_top8_kernel(DecArgs a) {
   }
   if (a.n == 0) {
     if (threadIdx.x == 0 && ld64(a.in + h.s.offsets) != 0) report_corrupt(a.status);
+    if (threadIdx.x < 64) check_codebooks(a, h.k, 256u);
     return;
   }
   const uint64_t tile = blockIdx.x;
@@ -1595,6 +1720,7 @@ __global__ __launch_bounds__(kThreads) void decode_top8_kernel(DecArgs a) {
       if (esc8) bf16_patch8(o, esc8, *reinterpret_cast<const uint2*>(vals + local));
       store_stream(out_t + 2 * local, o);
     }
+    if (tid < 64) check_codebooks(a, h.k, 256u);
     return;
   }
   uint16_t* out16 = reinterpret_cast<uint16_t*>(a.out);
@@ -1616,6 +1742,7 @@ __global__ __launch_bounds__(kThreads) void decode_top8_kernel(DecArgs a) {
     if (esc8) bf16_patch8(o, esc8, *reinterpret_cast<const uint2*>(vals + local));
     for (uint32_t j = 0; j < valid; ++j) out16[e0 + j] = (uint16_t)(pick4(o.x, o.y, o.z, o.w, j >> 1) >> (16 * (j & 1)));
   }
+  if (tid < 64) check_codebooks(a, h.k, 256u);
 }
 
 // Sets the exponent field of value j (0..7) of a decoded group to v.
@@ -1647,6 +1774,7 @@ __global__ __launch_bounds__(kThreads) void decode_sentinel_kernel(DecArgs a) {
   }
   if (a.n == 0) {
     if (threadIdx.x == 0 && ld64(a.in + h.s.offsets) != 0) report_corrupt(a.status);
+    if (threadIdx.x < 64) check_codebooks(a, h.k, 256u);
     return;
   }
   const uint32_t tid = threadIdx.x, wave = tid >> 6;
@@ -1754,6 +1882,7 @@ __global__ __launch_bounds__(kThreads) void decode_sentinel_kernel(DecArgs a) {
   if (bad) s_bad = 1;
   __syncthreads();
   if (tid == 0 && (s_bad || run != hi)) report_corrupt(a.status);
+  if (tid < 64) check_codebooks(a, h.k, 256u);
 }
 
 // ------------------------------------------------------------ host helpers

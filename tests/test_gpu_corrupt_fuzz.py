@@ -42,14 +42,21 @@ def _mutations(good: np.ndarray, n: int, code_bytes: int, rec: int, rng, count: 
     """(stream, in_bytes, label) cases, each damaged in one way: a byte of the
     offset table, of the codes or of the escape section; a record position
     nudged by one or two records swapped (position records only); E or S in
-    the header off by a little; fewer bytes than the stream holds."""
+    the header off by a little; fewer bytes than the stream holds; a codebook
+    entry repeated or replaced."""
     (off0, off1), (code0, code1), esc, E = _layout(good, n, code_bytes, rec)
     S = good.size
-    kinds = 7 if rec == 3 else 5
+    kinds = 8
     for i in range(count):
         t = good.copy()
         kind = i % kinds
-        if kind == 0:
+        if kind == 7:
+            # a codebook entry: a copy of another entry (a repeat) or any byte
+            # (out of range for E5M2 when >= 32, else still a valid codebook)
+            j = int(rng.integers(0, 16))
+            t[64 + j] = good[64 + (j + int(rng.integers(1, 16))) % 16] if rng.integers(0, 2) else rng.integers(0, 256)
+            yield t, S, "codebook byte"
+        elif kind == 0:
             t[rng.integers(off0, off1)] = rng.integers(0, 256)
             yield t, S, "offset byte"
         elif kind == 1:
@@ -65,11 +72,11 @@ def _mutations(good: np.ndarray, n: int, code_bytes: int, rec: int, rng, count: 
             yield t, S, "header E/S"
         elif kind == 4:
             yield t, S - int(rng.integers(1, 16)), "truncated"
-        elif kind == 5 and E:
+        elif kind == 5 and E and rec == 3:
             r = int(rng.integers(0, E))
             t[esc + 3 * r] = (int(t[esc + 3 * r]) + int(rng.choice([-1, 1]))) & 0xFF
             yield t, S, "position nudge"
-        elif kind == 6 and E > 1:
+        elif kind == 6 and E > 1 and rec == 3:
             r = int(rng.integers(0, E - 1))
             a, b = esc + 3 * r, esc + 3 * r + 3
             t[a:a + 3], t[b:b + 3] = good[b:b + 3], good[a:a + 3]
@@ -141,3 +148,53 @@ def test_variant_decoders_reject_exactly_what_the_oracle_rejects(variant, sigma)
            lambda dev, ib: sz.variant_decompress(variant, dev, n, in_bytes=ib),
            lambda t: O.variant_decompress_rc(variant, t, n)[0],
            lambda t: O.variant_decompress(variant, t, n))
+
+
+@pytest.mark.parametrize("dtype", [O.BF16, O.E5M2], ids=["bf16", "e5m2"])
+@pytest.mark.parametrize("n,k", [(3 * 65536 + 777, 5), (65536 + 5, 100), (0, 3)],
+                         ids=["unused-codebook", "more-codebooks-than-workgroups", "empty"])
+def test_every_codebook_is_validated(dtype, n, k):
+    """A stream is rejected when any of its K codebooks, used by a chunk or
+    not, repeats an entry or (E5M2) holds one of 32 or more, as the oracle's
+    validation rejects it; a codebook changed into another valid one still
+    decodes as the oracle decodes it.  With 100 codebooks and 9 tiles the
+    checks are spread over the workgroups several codebooks apiece."""
+    rng = np.random.default_rng(1000 * k + dtype)
+    xh = kvsynth.to_numpy_bits(kvsynth.random_bits(max(n, 1), dtype, seed=7, sigma=1.0))[:n]
+    vals = 256 if dtype == O.BF16 else 32
+    cbs = np.stack([rng.permutation(vals)[:16] for _ in range(k)]).astype(np.uint8)
+    good = O.compress(dtype, xh, cbs, 65536)
+    print(f"case codebooks dtype={dtype} n={n} K={k} S={good.size}", flush=True)
+    cases = []
+    for c in range(k):
+        for how in ("repeat", "out_of_range", "other_valid"):
+            if how == "out_of_range" and dtype == O.BF16:
+                continue
+            t = good.copy()
+            j = int(rng.integers(0, 16))
+            at = 64 + 16 * c + j
+            if how == "repeat":
+                t[at] = good[64 + 16 * c + (j + 1) % 16]
+            elif how == "out_of_range":
+                t[at] = int(rng.integers(32, 256))
+            else:
+                free = sorted(set(range(vals)) - set(int(v) for v in good[64 + 16 * c:64 + 16 * c + 16]))
+                t[at] = free[int(rng.integers(0, len(free)))]
+            cases.append((t, t.size, f"codebook {c} {how}"))
+    _check_codebook_cases(cases, dtype, n)
+
+
+def _check_codebook_cases(cases, dtype, n):
+    rejected = accepted = 0
+    for t, in_bytes, label in cases:
+        want = O.validate(t, dtype, n)
+        y, st = sz.decompress(torch.from_numpy(t).to(DEV), n, dtype, in_bytes=in_bytes)
+        torch.cuda.synchronize()
+        assert int(st.item()) == want, f"{label}: GPU status {int(st.item())}, oracle {want}"
+        if want == O.OK:
+            accepted += 1
+            assert np.array_equal(kvsynth.to_numpy_bits(y), O.decompress(t, dtype, n)), f"{label}: output differs"
+        else:
+            rejected += 1
+    print(f"  rejected {rejected}, still valid {accepted}", flush=True)
+    assert rejected > 0 and accepted > 0
