@@ -13,7 +13,8 @@
  *     negative SPLITZIP_E_* code); sizes are element or byte counts.
  *   - "d_" pointers are device memory (hipMalloc'd, or any memory the GPU
  *     can address); "h_" pointers are host memory.  The caller owns every
- *     buffer.  No call allocates device or host memory.
+ *     buffer.  No call allocates device or host memory (the pipelined
+ *     transfer creates HIP events for the duration of its call).
  *   - GPU work is enqueued on `stream` (NULL = the default stream) and is not
  *     waited for.  Host-detectable argument errors return at once and enqueue
  *     nothing.  A failed kernel launch returns SPLITZIP_E_HIP.
@@ -126,11 +127,19 @@ int splitzip_compress(int dtype, const void* d_in, size_t n_elems, const uint8_t
  *   d_out     n_elems elements, 16-byte aligned.
  *   d_status  optional (may be NULL), device int32, sticky: the caller sets
  *             it to SPLITZIP_OK (0) beforehand; the GPU writes
- *             SPLITZIP_E_CORRUPT into it if it finds the stream invalid (bad
- *             magic, version, dtype, n, sizes, codebook range, non-monotone
- *             chunk offsets, escape positions out of range or out of order)
- *             and never clears it, so one word can watch many calls.  d_out
- *             is then unspecified.  Every read stays inside in_bytes.
+ *             SPLITZIP_E_CORRUPT into it if it finds the stream invalid and
+ *             never clears it, so one word can watch many calls.  d_out is
+ *             then unspecified.  Invalid means: bad magic, version, dtype, n,
+ *             non-zero reserved header bytes, chunk count, codebook count
+ *             or segment size; E > n or
+ *             S != P + 3E or S > in_bytes; any of the K codebooks (used by a
+ *             chunk or not) with a repeated entry or, for E5M2, an entry of
+ *             32 or more; chunk offsets not starting at 0, decreasing, above
+ *             E, not ending at E, or giving a chunk more records than
+ *             elements; an escape position outside its chunk or not above
+ *             the previous one of the chunk; an escape value of 32 or more
+ *             (E5M2).  Every stream the encoder writes passes these checks,
+ *             and they are the oracle's.  Every read stays inside in_bytes.
  * Returns SPLITZIP_OK, SPLITZIP_E_INVALID or SPLITZIP_E_HIP. */
 int splitzip_decompress(const void* d_in, size_t in_bytes, int dtype, size_t n_elems, void* d_out,
                         int32_t* d_status, hipStream_t stream);
@@ -239,9 +248,12 @@ int splitzip_pipeline_sizes(int dtype, size_t n_elems, uint32_t n_codebooks, siz
  *   streams       four distinct streams: encode, device-to-host copies,
  *                 host-to-device copies, decode.
  * Blocking: the calling thread drives the pipeline and returns after all four
- * streams are synchronized; if no step can proceed for 60 s it returns
- * SPLITZIP_E_HIP.  On an error return, work already queued may
- * still run; synchronize the streams before reusing the buffers.  Returns
+ * streams are synchronized.  Between steps it polls for up to 40 us, then
+ * sleeps in the HIP runtime on the oldest outstanding step.  The call creates
+ * 4 * depth HIP events (blocking-sync, no timing) and destroys them before it
+ * returns; it allocates no device or host buffer.  On an error return, work
+ * already queued may still run; synchronize the streams before reusing the
+ * buffers.  Returns
  * SPLITZIP_OK, SPLITZIP_E_INVALID, SPLITZIP_E_CAPACITY, SPLITZIP_E_CODEBOOK
  * or SPLITZIP_E_HIP. */
 int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks,

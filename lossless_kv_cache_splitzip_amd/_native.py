@@ -142,8 +142,10 @@ def variant_compress(variant: int, x, codebooks, segment_elems: int = 0, out=Non
         out = torch.empty(cap, dtype=torch.uint8, device=x.device)
     if out_bytes is None:
         out_bytes = torch.zeros(1, dtype=torch.int64, device=x.device)
+    _device_buffer(out, "out", 0)  # its true size goes to the library, which checks the capacity
+    _out_bytes_word(out_bytes)
     rc = load().splitzip_variant_compress(variant, x.data_ptr(), x.numel(), cbs.ctypes.data, k, segment_elems,
-                                          out.data_ptr(), out.numel(), out_bytes.data_ptr(), _stream_handle(stream))
+                                          out.data_ptr(), _nbytes(out), out_bytes.data_ptr(), _stream_handle(stream))
     if rc != OK:
         raise SplitZipError(rc, "splitzip_variant_compress")
     return out, out_bytes
@@ -154,13 +156,16 @@ def variant_decompress(variant: int, stream_buf, n_elems: int, out=None, status=
     """Decode an ablation-variant stream held in a uint8 device tensor;
     returns (out, status) as ``decompress``."""
     import torch
-    if not stream_buf.is_cuda or not stream_buf.is_contiguous():
-        raise ValueError("stream must be a contiguous device tensor")
+    _device_buffer(stream_buf, "stream", 0)
     if out is None:
         out = torch.empty(n_elems, dtype=torch.int16, device=stream_buf.device)
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=stream_buf.device)
-    nbytes = stream_buf.numel() if in_bytes is None else in_bytes
+    _device_buffer(out, "out", 2 * n_elems)
+    _status_word(status)
+    nbytes = _nbytes(stream_buf) if in_bytes is None else int(in_bytes)
+    if nbytes > _nbytes(stream_buf):
+        raise ValueError(f"in_bytes {nbytes} exceeds the stream buffer ({_nbytes(stream_buf)} bytes)")
     rc = load().splitzip_variant_decompress(variant, stream_buf.data_ptr(), nbytes, n_elems, out.data_ptr(),
                                             status.data_ptr(), _stream_handle(stream))
     if rc != OK:
@@ -194,8 +199,10 @@ def calibrate_device(x, n_codebooks: int = 1, segment_elems: int = 0, out=None, 
         out = torch.empty((n_codebooks, 16), dtype=torch.uint8, device=x.device)
     if work is None:
         work = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _device_buffer(out, "out", 16 * n_codebooks)
+    _device_buffer(work, "work", need)
     rc = splitzip_calibrate_device(dtype, x.data_ptr(), x.numel(), segment_elems, n_codebooks, out.data_ptr(),
-                                   work.data_ptr(), work.numel(), _stream_handle(stream))
+                                   work.data_ptr(), _nbytes(work), _stream_handle(stream))
     if rc != OK:
         raise SplitZipError(rc, "splitzip_calibrate_device")
     return out
@@ -226,6 +233,48 @@ def splitzip_pipeline_transfer(dtype: int, d_in: int, n_elems: int, h_codebooks:
 
 
 # -------------------------------------------------------- torch conveniences
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _device_buffer(t, name: str, min_bytes: int):
+    """A contiguous device tensor of at least min_bytes bytes, else ValueError
+    (the library writes through its pointer for that many bytes)."""
+    if not hasattr(t, "is_cuda") or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if _nbytes(t) < min_bytes:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes, {min_bytes} needed")
+    return t
+
+
+def _word(t, name: str, dtypes, allow_host: bool):
+    """A one-or-more-element tensor of one of `dtypes` that the GPU may write:
+    device memory, or (allow_host) pinned host memory."""
+    if not hasattr(t, "dtype") or t.dtype not in dtypes:
+        raise ValueError(f"{name} must be a tensor of {' or '.join(str(d) for d in dtypes)}")
+    if t.numel() < 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous with at least one element")
+    if not t.is_cuda and not (allow_host and t.is_pinned()):
+        raise ValueError(f"{name} must be device memory" + (" or pinned host memory" if allow_host else ""))
+    return t
+
+
+def _out_bytes_word(t):
+    import torch
+    return _word(t, "out_bytes", (torch.int64, torch.uint64), allow_host=True)
+
+
+def _status_word(t):
+    import torch
+    return _word(t, "status", (torch.int32,), allow_host=False)
+
+
+def _elem_bytes(dtype: int) -> int:
+    return 2 if dtype == BF16 else 1
+
+
 def _host_bits(x, dtype: int) -> np.ndarray:
     if hasattr(x, "detach"):
         x = x.detach().cpu().numpy()
@@ -275,7 +324,9 @@ def compress(x, codebooks, segment_elems: int = 0, out=None, out_bytes=None, str
         out = torch.empty(cap, dtype=torch.uint8, device=x.device)
     if out_bytes is None:
         out_bytes = torch.zeros(1, dtype=torch.int64, device=x.device)
-    rc = splitzip_compress(dtype, x.data_ptr(), n, cbs, k, segment_elems, out.data_ptr(), out.numel(),
+    _device_buffer(out, "out", 0)  # its true size goes to the library, which checks the capacity
+    _out_bytes_word(out_bytes)
+    rc = splitzip_compress(dtype, x.data_ptr(), n, cbs, k, segment_elems, out.data_ptr(), _nbytes(out),
                            out_bytes.data_ptr(), _stream_handle(stream))
     if rc != OK:
         raise SplitZipError(rc, "splitzip_compress")
@@ -289,13 +340,18 @@ def decompress(stream_buf, n_elems: int, dtype: int, out=None, status=None, in_b
     E_CORRUPT once a corrupt stream was seen (a passed-in ``status`` is not
     cleared first).  Nothing is synchronized."""
     import torch
-    if not stream_buf.is_cuda or not stream_buf.is_contiguous():
-        raise ValueError("stream must be a contiguous device tensor")
+    if dtype not in (BF16, FP8_E5M2):
+        raise ValueError(f"unknown dtype {dtype}")
+    _device_buffer(stream_buf, "stream", 0)
     if out is None:
         out = torch.empty(n_elems, dtype=torch.int16 if dtype == BF16 else torch.uint8, device=stream_buf.device)
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=stream_buf.device)
-    nbytes = stream_buf.numel() * stream_buf.element_size() if in_bytes is None else in_bytes
+    _device_buffer(out, "out", n_elems * _elem_bytes(dtype))
+    _status_word(status)
+    nbytes = _nbytes(stream_buf) if in_bytes is None else int(in_bytes)
+    if nbytes > _nbytes(stream_buf):
+        raise ValueError(f"in_bytes {nbytes} exceeds the stream buffer ({_nbytes(stream_buf)} bytes)")
     rc = splitzip_decompress(stream_buf.data_ptr(), nbytes, dtype, n_elems, out.data_ptr(), status.data_ptr(),
                              _stream_handle(stream))
     if rc != OK:
@@ -333,11 +389,19 @@ class Pipeline:
     """Buffers and streams of a chunk-pipelined transfer (device work area,
     coherent pinned host link buffer, four streams), reusable across calls of
     the same shape.  ``transfer(x, out)`` moves ``x`` into ``out`` through
-    the link, compressed or raw, and returns the bytes each group sent."""
+    the link, compressed or raw, and returns the bytes each group sent.
+
+    The pinned link buffer is released by ``close()`` (or at the end of a
+    ``with`` block), after the four streams have drained; a finalizer makes
+    no HIP call, so a pipeline never closed keeps its buffer until the
+    process ends."""
+
+    DRAIN_S = 60.0  # longest wait for the streams before close() gives up
 
     def __init__(self, dtype: int, n_elems: int, codebooks, segment_elems: int, group_elems: int, depth: int,
                  device=None, host_flags: int = HIP_HOST_MALLOC_COHERENT):
         import torch
+        self._link = ctypes.c_void_p(0)
         self.dtype, self.n, self.seg, self.group, self.depth = dtype, n_elems, segment_elems, group_elems, depth
         self.cbs = np.ascontiguousarray(np.asarray(codebooks, dtype=np.uint8)).reshape(-1, 16)
         self.work_bytes, self.link_bytes = splitzip_pipeline_sizes(dtype, n_elems, self.cbs.shape[0], segment_elems,
@@ -345,23 +409,60 @@ class Pipeline:
         self.groups = -(-n_elems // group_elems)
         self.slot = (self.link_bytes - (-(-8 * self.groups // 256) * 256)) // depth
         self.work = torch.empty(self.work_bytes, dtype=torch.uint8, device=device)
-        self._link = ctypes.c_void_p(0)
         rc = _hip_runtime().hipHostMalloc(ctypes.byref(self._link), self.link_bytes, host_flags)
         if rc != 0 or not self._link.value:
+            self._link = ctypes.c_void_p(0)
             raise RuntimeError(f"hipHostMalloc failed ({rc})")
+        self.streams = [torch.cuda.Stream(device=device) for _ in range(4)]
         if self.work.data_ptr() % 256 or self._link.value % 256:
+            self.close()
             raise RuntimeError("pipeline buffers are not 256-byte aligned")
         self.link = np.ctypeslib.as_array((ctypes.c_uint8 * self.link_bytes).from_address(self._link.value))
-        self.streams = [torch.cuda.Stream(device=device) for _ in range(4)]
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+        return False
+
+    def _drain(self) -> bool:
+        """Wait (at most DRAIN_S seconds) until the four streams are idle."""
+        import time
+        t_end = time.monotonic() + self.DRAIN_S
+        while not all(s.query() for s in self.streams):
+            if time.monotonic() > t_end:
+                return False
+            time.sleep(1e-4)
+        return True
+
+    def close(self):
+        """Release the pinned link buffer once no queued copy can still use it.
+        If the streams do not drain in time the buffer is left allocated
+        (freeing memory a copy engine may still write would be worse)."""
+        if not self._link.value:
+            return
+        if self._drain():
+            _hip_runtime().hipHostFree(self._link)
+        self._link = ctypes.c_void_p(0)
+        self.link = None
 
     def __del__(self):
         if getattr(self, "_link", None) is not None and self._link.value:
-            _hip_runtime().hipHostFree(self._link)
-            self._link = None
+            import warnings
+            warnings.warn("Pipeline was not closed; its pinned link buffer stays allocated until exit",
+                          ResourceWarning, stacklevel=2)
 
     def transfer(self, x, out, compress: bool = True, status=None):
-        if not x.is_contiguous() or not out.is_contiguous() or x.numel() != self.n or out.numel() != self.n:
-            raise ValueError("x and out must be contiguous with the planned element count")
+        if not self._link.value:
+            raise RuntimeError("pipeline is closed")
+        nb = self.n * _elem_bytes(self.dtype)
+        _device_buffer(x, "x", nb)
+        _device_buffer(out, "out", nb)
+        if x.numel() * x.element_size() != nb or out.numel() * out.element_size() != nb:
+            raise ValueError("x and out must hold exactly the planned elements")
+        if status is not None:
+            _status_word(status)
         sizes = np.zeros(self.groups, dtype=np.uint64)
         rc = splitzip_pipeline_transfer(self.dtype, x.data_ptr(), self.n, self.cbs, self.cbs.shape[0], self.seg,
                                         self.group, self.depth, compress, self.work.data_ptr(), self.work_bytes,
@@ -369,6 +470,10 @@ class Pipeline:
                                         None if status is None else status.data_ptr(), sizes,
                                         [s.cuda_stream for s in self.streams])
         if rc != OK:
+            # work the call queued before it failed may still be running on
+            # the four streams: let it finish before the caller reuses x, out
+            # or this pipeline's buffers
+            self._drain()
             raise SplitZipError(rc, "splitzip_pipeline_transfer")
         return sizes
 

@@ -9,12 +9,16 @@
 // the same pipeline, the baseline of that comparison.
 //
 // The calling thread drives the pipeline as a state machine: it queues each
-// step of a group once the host has seen, by polling events, that the step's
-// inputs are complete and its ring slot is free, so no stream ever waits on
-// another (cross-stream event waits cost up to a millisecond each between
-// copy-engine queues on this system).  A compressed group's size exists only
-// on the device: the encoder writes it into the pinned link buffer, where
-// the host reads it before queuing the group's copies.
+// step of a group once the host has seen, by querying events, that the
+// step's inputs are complete and its ring slot is free, so no stream ever
+// waits on another (cross-stream event waits cost up to a millisecond each
+// between copy-engine queues on this system).  When no step can be queued,
+// the thread polls for a short while (the next step is often moments away)
+// and then sleeps in the HIP runtime on the oldest outstanding step's event
+// (blocking-sync events), so it does not hold a host core for the whole
+// transfer.  A compressed group's size exists only on the device: the
+// encoder writes it into the pinned link buffer, where the host reads it
+// before queuing the group's copies.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -109,8 +113,15 @@ int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, cons
   Events ev;
   ev.e.assign(4 * (size_t)depth, nullptr);
   for (hipEvent_t& x : ev.e)
-    if (hipEventCreateWithFlags(&x, hipEventDisableTiming) != hipSuccess) return SPLITZIP_E_HIP;
+    if (hipEventCreateWithFlags(&x, hipEventDisableTiming | hipEventBlockingSync) != hipSuccess)
+      return SPLITZIP_E_HIP;
+  std::vector<uint64_t> seq(4 * (size_t)depth, 0);  // order in which the events were recorded
+  uint64_t recorded = 0;
   auto E = [&](int kind, uint64_t g) { return ev.e[4 * (g % depth) + kind]; };
+  auto record = [&](int kind, uint64_t g, hipStream_t st) {
+    seq[4 * (g % depth) + kind] = ++recorded;
+    return hipEventRecord(E(kind, g), st) == hipSuccess;
+  };
   hipError_t qerr = hipSuccess;
   auto done = [&](int kind, uint64_t g) {  // step `kind` of group g has completed
     const hipError_t q = hipEventQuery(E(kind, g));
@@ -136,10 +147,28 @@ int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, cons
   // next group to take each step: compress, copy out, copy back, decode
   uint64_t nc = 0, nd = 0, nh = 0, nx = 0;
   const uint64_t G = p.groups;
-  // a step that makes no progress for this long means the device stopped
-  // answering: give up rather than spin forever
-  constexpr auto kStall = std::chrono::seconds(60);
+  // after a step was queued, poll this long before sleeping on an event
+  constexpr auto kPoll = std::chrono::microseconds(40);
   auto last_progress = std::chrono::steady_clock::now();
+  // The oldest recorded event, among those the queue conditions below wait
+  // for, that has not completed: waiting on it never waits on work that
+  // was not queued.  -1 if there is none.
+  auto oldest_pending = [&]() -> int {
+    int best = -1;
+    auto consider = [&](int kind, uint64_t g, bool recorded_already) {
+      if (!recorded_already) return;
+      const int i = 4 * (int)(g % depth) + kind;
+      if (best >= 0 && seq[i] >= seq[best]) return;
+      if (!done(kind, g)) best = i;
+    };
+    if (nc < G && nc >= depth) consider(1, nc - depth, nd > nc - depth);
+    if (nd < nc) consider(0, nd, true);
+    if (nd < nc && nd >= depth) consider(2, nd - depth, nh > nd - depth);
+    if (nh < nd) consider(1, nh, true);
+    if (compress && nh < nd && nh >= depth) consider(3, nh - depth, nx > nh - depth);
+    if (compress && nx < nh) consider(2, nx, true);
+    return best;
+  };
   while (compress ? nx < G : nh < G) {
     bool progress = false;
     // compress g: its send slot is free once group g - depth was copied out
@@ -157,7 +186,7 @@ int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, cons
       } else {
         sizes[g] = group_n(g) * elem;
       }
-      if (hipEventRecord(E(0, g), s_enc) != hipSuccess) return SPLITZIP_E_HIP;
+      if (!record(0, g, s_enc)) return SPLITZIP_E_HIP;
       ++nc, progress = true;
     }
     // copy g to host: once compressed, and once group g - depth has been
@@ -172,7 +201,7 @@ int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, cons
       if (h_group_bytes) h_group_bytes[g] = bytes;
       const void* src = compress ? static_cast<const void*>(send + slot * p.slot) : in + g * group_elems * elem;
       if (hipMemcpyAsync(host + slot * p.slot, src, moved[g], hipMemcpyDeviceToHost, s_d2h) != hipSuccess ||
-          hipEventRecord(E(1, g), s_d2h) != hipSuccess)
+          !record(1, g, s_d2h))
         return SPLITZIP_E_HIP;
       ++nd, progress = true;
     }
@@ -182,7 +211,7 @@ int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, cons
       const uint64_t g = nh, slot = g % depth;
       void* dst = compress ? static_cast<void*>(recv + slot * p.slot) : out + g * group_elems * elem;
       if (hipMemcpyAsync(dst, host + slot * p.slot, moved[g], hipMemcpyHostToDevice, s_h2d) != hipSuccess ||
-          hipEventRecord(E(2, g), s_h2d) != hipSuccess)
+          !record(2, g, s_h2d))
         return SPLITZIP_E_HIP;
       ++nh, progress = true;
     }
@@ -192,15 +221,20 @@ int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, cons
       rc = splitzip_decompress(recv + slot * p.slot, moved[g], dtype, group_n(g), out + g * group_elems * elem,
                                d_status, s_dec);
       if (rc != SPLITZIP_OK) return rc;
-      if (hipEventRecord(E(3, g), s_dec) != hipSuccess) return SPLITZIP_E_HIP;
+      if (!record(3, g, s_dec)) return SPLITZIP_E_HIP;
       ++nx, progress = true;
     }
     if (qerr != hipSuccess) return SPLITZIP_E_HIP;
     if (progress) {
       last_progress = std::chrono::steady_clock::now();
-    } else {
-      if (std::chrono::steady_clock::now() - last_progress > kStall) return SPLITZIP_E_HIP;
+    } else if (std::chrono::steady_clock::now() - last_progress < kPoll) {
       std::this_thread::yield();
+    } else {
+      const int i = oldest_pending();
+      if (qerr != hipSuccess) return SPLITZIP_E_HIP;
+      // none pending: a condition just turned true, the next pass queues it
+      if (i >= 0 && hipEventSynchronize(ev.e[i]) != hipSuccess) return SPLITZIP_E_HIP;
+      last_progress = std::chrono::steady_clock::now();
     }
   }
   for (int i = 0; i < 4; ++i)

@@ -42,6 +42,13 @@ def _run(name, group, depth, layers=None, tokens=None, trim=0, check_streams=Tru
     x = wl.data[:wl.n - trim].contiguous() if trim else wl.data
     n = x.numel()
     p = sz.Pipeline(dtype, n, cbs, seg, group, depth, device="cuda")
+    try:
+        return _transfer_and_check(p, x, n, dtype, cbs, seg, group, depth, name, check_streams)
+    finally:
+        p.close()
+
+
+def _transfer_and_check(p, x, n, dtype, cbs, seg, group, depth, name, check_streams):
     out = torch.empty_like(x)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     sizes = p.transfer(x, out, compress=True, status=status)
