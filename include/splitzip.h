@@ -70,7 +70,8 @@ enum {
   SPLITZIP_E_CAPACITY = -2, /* output buffer smaller than splitzip_max_compressed_size() */
   SPLITZIP_E_CODEBOOK = -3, /* codebook entries repeated or out of range for the dtype */
   SPLITZIP_E_CORRUPT = -4,  /* stream fails validation (reported through d_status) */
-  SPLITZIP_E_HIP = -5       /* a HIP launch failed */
+  SPLITZIP_E_HIP = -5,      /* a HIP launch failed */
+  SPLITZIP_E_TOO_LARGE = -6 /* input beyond splitzip_compress_static's limit */
 };
 
 /* Offline calibration (technical summary, "Metodologia / Codificacion de
@@ -146,6 +147,28 @@ int splitzip_decompress(const void* d_in, size_t in_bytes, int dtype, size_t n_e
 
 /* Static text for a status code. */
 const char* splitzip_status_string(int status);
+
+/* splitzip_compress for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The encoder's workspace is the library's own device array
+ * (about 2 MiB per GPU, kept until the process ends), so d_out only needs
+ * room for the largest stream:
+ *   out_capacity >= A(P + 3 n_elems), P as in the layout above (n_elems
+ *   escapes; splitzip_max_compressed_size minus the workspace).
+ * Limits: n_elems <= 1024 * 8192 (BF16, 16 MiB) or 1024 * 16384 (E5M2,
+ * 16 MiB), else SPLITZIP_E_TOO_LARGE; n_codebooks <= 128.  Other arguments,
+ * errors and the stream are those of splitzip_compress: the stream is byte
+ * for byte the one splitzip_compress writes.  One kernel launch (plus a
+ * one-word clear kernel at a device's first call); no hipMalloc, hipFree,
+ * memset or host synchronization, so it can be captured in a HIP graph.
+ * Every call on one GPU shares that GPU's workspace: calls that overlap on
+ * one GPU (two streams, two host threads) race and may write wrong streams;
+ * serialize them.  The stream passed must belong to the current device.
+ * Returns SPLITZIP_OK, SPLITZIP_E_INVALID, SPLITZIP_E_CODEBOOK,
+ * SPLITZIP_E_CAPACITY, SPLITZIP_E_TOO_LARGE or SPLITZIP_E_HIP. */
+int splitzip_compress_static(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks,
+                             uint32_t n_codebooks, size_t segment_elems, void* d_out, size_t out_capacity,
+                             uint64_t* d_out_bytes, hipStream_t stream);
 
 /* ---- Ablation variants (BF16) ---------------------------------------------
  * The two designs the pages measure against the top-16 codec (technical

@@ -12,6 +12,7 @@ from ._native import (  # noqa: F401
     E_CORRUPT,
     E_HIP,
     E_INVALID,
+    E_TOO_LARGE,
     EXPORTS,
     FP8_E5M2,
     LIB_PATH,
@@ -22,12 +23,14 @@ from ._native import (  # noqa: F401
     SplitZipError,
     calibrate_device,
     compress,
+    compress_static,
     decompress,
     load,
     splitzip_calibrate,
     splitzip_calibrate_device,
     splitzip_calibrate_device_work_bytes,
     splitzip_compress,
+    splitzip_compress_static,
     splitzip_decompress,
     splitzip_max_compressed_size,
     splitzip_pipeline_sizes,

@@ -22,6 +22,7 @@ E_CAPACITY = -2
 E_CODEBOOK = -3
 E_CORRUPT = -4
 E_HIP = -5
+E_TOO_LARGE = -6
 VARIANT_TOP15_SENTINEL = 1
 VARIANT_TOP8 = 2
 
@@ -38,6 +39,7 @@ EXPORTS = (
     "splitzip_calibrate_device",
     "splitzip_pipeline_sizes",
     "splitzip_pipeline_transfer",
+    "splitzip_compress_static",
 )
 
 _lib = None
@@ -85,6 +87,8 @@ def load():
     lib.splitzip_pipeline_sizes.restype = i32
     lib.splitzip_pipeline_transfer.argtypes = [i32, vp, sz, vp, u32, sz, sz, u32, i32, vp, sz, vp, sz, vp, vp, vp, vp]
     lib.splitzip_pipeline_transfer.restype = i32
+    lib.splitzip_compress_static.argtypes = [i32, vp, sz, vp, u32, sz, vp, sz, vp, vp]
+    lib.splitzip_compress_static.restype = i32
     _lib = lib
     return lib
 
@@ -115,6 +119,15 @@ def splitzip_compress(dtype: int, d_in: int, n_elems: int, h_codebooks: np.ndarr
     return int(load().splitzip_compress(dtype, d_in or None, n_elems, cbs.ctypes.data, n_codebooks,
                                         segment_elems, d_out or None, out_capacity, d_out_bytes or None,
                                         stream or None))
+
+
+def splitzip_compress_static(dtype: int, d_in: int, n_elems: int, h_codebooks: np.ndarray, n_codebooks: int,
+                             segment_elems: int, d_out: int, out_capacity: int, d_out_bytes: int | None,
+                             stream: int | None) -> int:
+    cbs = np.ascontiguousarray(h_codebooks, dtype=np.uint8)
+    return int(load().splitzip_compress_static(dtype, d_in or None, n_elems, cbs.ctypes.data, n_codebooks,
+                                               segment_elems, d_out or None, out_capacity, d_out_bytes or None,
+                                               stream or None))
 
 
 def splitzip_decompress(d_in: int, in_bytes: int, dtype: int, n_elems: int, d_out: int,
@@ -330,6 +343,29 @@ def compress(x, codebooks, segment_elems: int = 0, out=None, out_bytes=None, str
                            out_bytes.data_ptr(), _stream_handle(stream))
     if rc != OK:
         raise SplitZipError(rc, "splitzip_compress")
+    return out, out_bytes
+
+
+def compress_static(x, codebooks, segment_elems: int = 0, out=None, out_bytes=None, stream=None):
+    """``compress`` through splitzip_compress_static: one launch, the
+    workspace in the library's own device memory, for inputs of at most
+    1024 tiles (16 MiB).  Calls that overlap on one GPU race."""
+    import torch
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor")
+    dtype = _dtype_of(x)
+    cbs = np.ascontiguousarray(np.asarray(codebooks, dtype=np.uint8)).reshape(-1, 16)
+    k = cbs.shape[0]
+    if out is None:  # room for the largest stream (and more: the workspace splitzip_compress needs)
+        out = torch.empty(splitzip_max_compressed_size(dtype, x.numel(), k), dtype=torch.uint8, device=x.device)
+    if out_bytes is None:
+        out_bytes = torch.zeros(1, dtype=torch.int64, device=x.device)
+    _device_buffer(out, "out", 0)  # the library checks the capacity
+    _out_bytes_word(out_bytes)
+    rc = splitzip_compress_static(dtype, x.data_ptr(), x.numel(), cbs, k, segment_elems, out.data_ptr(),
+                                  _nbytes(out), out_bytes.data_ptr(), _stream_handle(stream))
+    if rc != OK:
+        raise SplitZipError(rc, "splitzip_compress_static")
     return out, out_bytes
 
 

@@ -1,0 +1,135 @@
+"""splitzip_compress_static, the compress entry point that allocates nothing
+(its workspace is the library's own device array): called through the C ABI,
+its stream equals splitzip_compress's byte for byte, on two calls in a row
+(the second with a smaller input), at the size limit, with escape-heavy tiles
+(placed by re-encoding), several codebooks, the exact minimum capacity, an
+empty input, and replayed from a HIP graph.  Sizes beyond its limit are
+refused before any GPU work."""
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+sz = pytest.importorskip("lossless_kv_cache_splitzip_amd")
+DEV = "cuda"
+
+
+def _min_capacity(dtype, n, k):
+    """Bytes of the largest stream, rounded up to 256 (the oracle's layout)."""
+    return (O.max_size(dtype, n, k) + 255) // 256 * 256
+
+
+def _reference(x, cbs, seg):
+    """splitzip_compress's stream of x (the existing entry point)."""
+    out, nb = sz.compress(x, cbs, seg)
+    torch.cuda.synchronize()
+    return out[:int(nb.item())].clone()
+
+
+def _static(x, cbs, seg, cap=None, fill=0xA5):
+    """splitzip_compress_static into a buffer of cap bytes (pre-filled, so
+    bytes the call fails to write show up)."""
+    dtype = sz._native._dtype_of(x)
+    k = np.asarray(cbs).reshape(-1, 16).shape[0]
+    cap = cap or _min_capacity(dtype, x.numel(), k)
+    out = torch.full((cap,), fill, dtype=torch.uint8, device=DEV)
+    nb = torch.zeros(1, dtype=torch.int64, device=DEV)
+    rc = sz.splitzip_compress_static(dtype, x.data_ptr(), x.numel(), np.ascontiguousarray(cbs, dtype=np.uint8), k, seg,
+                                     out.data_ptr(), cap, nb.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return rc, out, int(nb.item())
+
+
+def _check(x, cbs, seg, label):
+    print(f"case static {label} n={x.numel()} k={np.asarray(cbs).reshape(-1, 16).shape[0]}", flush=True)
+    want = _reference(x, cbs, seg)
+    rc, out, nb = _static(x, cbs, seg)
+    assert rc == sz.OK, sz.status_string(rc)
+    assert nb == want.numel(), (nb, want.numel())
+    assert torch.equal(out[:nb], want), f"{label}: stream differs from splitzip_compress's"
+    dtype = sz._native._dtype_of(x)
+    y, st = sz.decompress(out[:nb], x.numel(), dtype)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and torch.equal(y.view(torch.uint8), x.view(torch.uint8))
+    return out[:nb]
+
+
+def _layer(name, **kw):
+    wl = kvsynth.make(name, device=DEV, **kw)
+    cbs = np.stack([sz.splitzip_calibrate(wl.spec.dtype, kvsynth.to_numpy_bits(c)) for c in wl.calib])
+    return wl, cbs
+
+
+def test_two_calls_in_a_row_second_smaller_bf16():
+    wl, cbs = _layer("kv_layer_bf16")  # 2,097,152 values: 256 tiles
+    got = _check(wl.data, cbs[:1], 0, "one layer")
+    xh = kvsynth.to_numpy_bits(wl.data)
+    assert np.array_equal(got.cpu().numpy(), O.compress(O.BF16, xh, cbs[:1]))
+    small = wl.data[:300_001].contiguous()  # 37 tiles, ragged tail
+    _check(small, cbs[:1], 0, "smaller, ragged")
+
+
+def test_two_calls_in_a_row_second_smaller_e5m2():
+    wl, cbs = _layer("llama3_70b_kv_e5m2", layers=3, tokens=1024)  # 3 layers of 2,097,152 values
+    seg = wl.segment_elems
+    _check(wl.data, cbs, seg, "3 layers, 3 codebooks")
+    _check(wl.data[:2 * seg + 77].contiguous(), cbs, seg, "smaller, ragged")
+
+
+def test_size_limit():
+    x = kvsynth.random_bits(1024 * 8192, kvsynth.BF16, seed=3, device=DEV)  # exactly 1024 tiles
+    cb = O.calibrate(O.BF16, kvsynth.to_numpy_bits(x[:100_000]))
+    _check(x, cb, 0, "1024 tiles")
+    big = kvsynth.random_bits(1024 * 8192 + 1, kvsynth.BF16, seed=4, device=DEV)
+    rc, _, _ = _static(big, cb, 0, cap=_min_capacity(O.BF16, big.numel(), 1))
+    assert rc == sz.E_TOO_LARGE
+
+
+def test_escape_heavy_tiles_and_capacity():
+    # uniform bit patterns: every tile holds far more escapes than its
+    # staging slot, so the last workgroup encodes them again
+    x = kvsynth.random_bits(600_001, kvsynth.BF16, seed=5, device=DEV, kind="uniform_bits")
+    cb = O.calibrate(O.BF16, kvsynth.to_numpy_bits(x[:5000]))
+    _check(x, cb, 0, "uniform bits")
+    cap = _min_capacity(O.BF16, x.numel(), 1)
+    rc, _, _ = _static(x, cb, 0, cap=cap - 1)
+    assert rc == sz.E_CAPACITY
+    rc, _, _ = _static(x, cb, 0, cap=cap)
+    assert rc == sz.OK
+
+
+def test_empty_input():
+    x = torch.empty(0, dtype=torch.int16, device=DEV)
+    cb = np.arange(16, dtype=np.uint8)
+    rc, out, nb = _static(x, cb, 0)
+    assert rc == sz.OK
+    assert np.array_equal(out[:nb].cpu().numpy(), O.compress(O.BF16, np.zeros(0, np.uint16), cb))
+
+
+def test_graph_replays_match_eager_calls():
+    wl, cbs = _layer("kv_layer_bf16", tokens=512)
+    x = wl.data.clone()
+    cap = _min_capacity(O.BF16, x.numel(), 1)
+    out = torch.empty(cap, dtype=torch.uint8, device=DEV)
+    nb = torch.zeros(1, dtype=torch.int64, device=DEV)
+    cb = np.ascontiguousarray(cbs[:1])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # eager warm-up on the capture stream
+        assert sz.compress_static(x, cb, out=out, out_bytes=nb)[0] is out
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sz.compress_static(x, cb, out=out, out_bytes=nb)
+    torch.cuda.synchronize()
+    for r in range(4):
+        x.copy_(kvsynth.random_bits(x.numel(), kvsynth.BF16, seed=100 + r, device=DEV))
+        torch.cuda.synchronize()
+        want = _reference(x, cb, 0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(nb.item()) == want.numel() and torch.equal(out[:want.numel()], want), f"replay {r}"
