@@ -150,20 +150,21 @@ const char* splitzip_status_string(int status);
 
 /* splitzip_compress for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc.  The encoder's workspace is the library's own device array
- * (about 2 MiB per GPU, kept until the process ends), so d_out only needs
- * room for the largest stream:
- *   out_capacity >= A(P + 3 n_elems), P as in the layout above (n_elems
- *   escapes; splitzip_max_compressed_size minus the workspace).
- * Limits: n_elems <= 1024 * 8192 (BF16, 16 MiB) or 1024 * 16384 (E5M2,
- * 16 MiB), else SPLITZIP_E_TOO_LARGE; n_codebooks <= 128.  Other arguments,
- * errors and the stream are those of splitzip_compress: the stream is byte
- * for byte the one splitzip_compress writes.  One kernel launch (plus a
- * one-word clear kernel at a device's first call); no hipMalloc, hipFree,
- * memset or host synchronization, so it can be captured in a HIP graph.
- * Every call on one GPU shares that GPU's workspace: calls that overlap on
- * one GPU (two streams, two host threads) race and may write wrong streams;
- * serialize them.  The stream passed must belong to the current device.
+ * hipMalloc.  The same launches as splitzip_compress, with the encoder's
+ * workspace (per-tile escape counts and record staging slots) in the
+ * library's own device array (about 4 MiB per GPU, kept until the process
+ * ends) instead of the tail of d_out, so d_out only needs room for the
+ * largest stream:
+ *   out_capacity >= A(P + 3 n_elems), P as in the layout above with
+ *   n_elems escapes (splitzip_max_compressed_size minus the workspace).
+ * Limit: n_elems <= 2048 * 8192 (BF16) or 2048 * 16384 (E5M2), 32 MiB of
+ * input, else SPLITZIP_E_TOO_LARGE.  Other arguments, errors and the stream
+ * are those of splitzip_compress: the stream is byte for byte the one
+ * splitzip_compress writes.  No hipMalloc, hipFree, memset or host
+ * synchronization, so it can be captured in a HIP graph.  Every call on one
+ * GPU shares that GPU's workspace: calls that overlap on one GPU (two
+ * streams, two host threads) race and may write wrong streams; serialize
+ * them.  The stream passed must belong to the current device.
  * Returns SPLITZIP_OK, SPLITZIP_E_INVALID, SPLITZIP_E_CODEBOOK,
  * SPLITZIP_E_CAPACITY, SPLITZIP_E_TOO_LARGE or SPLITZIP_E_HIP. */
 int splitzip_compress_static(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks,
@@ -271,10 +272,11 @@ int splitzip_pipeline_sizes(int dtype, size_t n_elems, uint32_t n_codebooks, siz
  *   streams       four distinct streams: encode, device-to-host copies,
  *                 host-to-device copies, decode.
  * Blocking: the calling thread drives the pipeline and returns after all four
- * streams are synchronized.  Between steps it polls for up to 40 us, then
- * sleeps in the HIP runtime on the oldest outstanding step.  The call creates
- * 4 * depth HIP events (blocking-sync, no timing) and destroys them before it
- * returns; it allocates no device or host buffer.  On an error return, work
+ * streams are synchronized.  When no step can be queued it polls for 40 us,
+ * then naps 20 us between polls; if no step can proceed for 60 s it returns
+ * SPLITZIP_E_HIP.  The call creates 4 * depth HIP events (no timing) and
+ * destroys them before it returns; it allocates no device or host buffer.
+ * On an error return, work
  * already queued may still run; synchronize the streams before reusing the
  * buffers.  Returns
  * SPLITZIP_OK, SPLITZIP_E_INVALID, SPLITZIP_E_CAPACITY, SPLITZIP_E_CODEBOOK

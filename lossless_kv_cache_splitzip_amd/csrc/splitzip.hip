@@ -293,7 +293,6 @@ struct EncArgs {
   uint32_t cb_args;       // codebooks read from prep.cbs (all of them fit), else from the stream
   uint32_t prep_in;       // header, codebooks and padding written by: 0 prep_kernel, 1 encode_sums, 2 encode_place
   uint32_t sums_in_place; // at most 64 blocks: encode_place sums the lower tiles itself, encode_sums is not launched
-  uint32_t* arrivals;     // one-launch encode: tiles of the running call that have finished (static scratch)
   PrepArgs prep;          // the header work folded into a later launch (prep_in 1 or 2)
 };
 
@@ -1102,57 +1101,25 @@ __global__ __launch_bounds__(kThreads) void encode_place_e5m2_kernel(EncArgs a) 
 __global__ __launch_bounds__(kThreads) void encode_place_sentinel_kernel(EncArgs a) { encode_place<true, kSentinel>(a); }
 __global__ __launch_bounds__(kThreads) void encode_place_top8_kernel(EncArgs a) { encode_place<true, kTop8>(a); }
 
-// ------------------------------------------------- one-launch encode (static scratch)
+// ------------------------------------------------- static-scratch workspace
 //
-// For inputs of at most kStaticMaxTiles tiles, with the workspace in the
-// library's own device memory (`scratch`, below) instead of the caller's
-// buffer.  One launch of tiles + 1 workgroups; no workgroup waits on another:
-//   tile workgroups  dense_tile (as encode_dense), then count themselves in
-//                    on an arrival counter; the one that arrives last places
-//                    every tile's records (place_range over all tiles, base 0)
-//                    and sets the counter back to 0 for the next call;
-//   last workgroup   header, codebooks and padding (prep_work).
-// The counter starts at 0 (static storage, and a clear kernel at a device's
-// first call) and every call leaves it at 0.  Calls that overlap on one GPU
-// share the counter and the staging slots, so they race.
-constexpr uint32_t kStaticMaxTiles = 1024;  // 8M BF16 or 16M E5M2 elements
-constexpr uint32_t kStaticCountAt = 64;     // words: counter at 0, tile counts, staging slots
-constexpr uint32_t kStaticStageAt = kStaticCountAt + kStaticMaxTiles;
+// splitzip_compress_static runs the same launches as splitzip_compress, with
+// the encoder's workspace (tile counts and staging slots; inputs of at most
+// kStaticMaxTiles tiles need no block sums) in the library's own device
+// array instead of the tail of the caller's buffer.  Every word a call reads
+// there it wrote first (counts of all its tiles, the slots of the tiles it
+// staged), so nothing needs clearing between calls; calls that overlap on
+// one GPU share the array, so they race.
+constexpr uint32_t kStaticMaxTiles = 2048;  // 16M BF16 or 32M E5M2 elements (32 MiB)
+constexpr uint32_t kStaticStageAt = kStaticMaxTiles;  // words: tile counts, then staging slots
 constexpr uint64_t kStaticWords = kStaticStageAt + (uint64_t)kStaticMaxTiles * stage_slot(kMain);
 
-// The library's encoder workspace for the one-launch encode, one copy per
-// GPU (about 2 MiB).  Host code reaches it only through the address that
-// hipGetSymbolAddress returns for the current device.
+static_assert(kStaticMaxTiles <= 64 * kBlockTiles, "inputs within the limit take the path without block sums");
+
+// The encoder workspace of splitzip_compress_static, one copy per GPU (about
+// 4 MiB).  Host code reaches it only through the address hipGetSymbolAddress
+// returns with that GPU current.
 static __device__ __align__(256) uint32_t scratch[kStaticWords];
-
-template <bool kBf16>
-__device__ void encode_one_launch(const EncArgs& a) {
-  __shared__ EncShared sh;
-  __shared__ DenseLds<kBf16> dl;
-  __shared__ PlaceLds<kStaticMaxTiles> psh;
-  __shared__ uint32_t s_last;
-  if (blockIdx.x == gridDim.x - 1) {  // the launch's extra workgroup
-    prep_work(a.prep, 0, 1);
-    return;
-  }
-  dense_tile<kBf16>(a, sh, dl, blockIdx.x);
-  __syncthreads();  // every thread's count and staged-record stores are done
-  if (threadIdx.x == 0) {
-    __threadfence();  // release: they reach device scope before this tile is counted
-    s_last = atomicAdd(a.arrivals, 1u) == (uint32_t)a.n_tiles - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;  // same in the workgroup
-  __threadfence();      // acquire: every other tile's count and records
-  if (threadIdx.x == 0) *a.arrivals = 0;  // every tile has arrived: ready for the next call
-  place_range<kBf16, kMain, kStaticMaxTiles>(a, psh, sh, 0, (uint32_t)a.n_tiles, 0);
-}
-
-__global__ __launch_bounds__(kThreads) void encode_one_launch_bf16_kernel(EncArgs a) { encode_one_launch<true>(a); }
-__global__ __launch_bounds__(kThreads) void encode_one_launch_e5m2_kernel(EncArgs a) { encode_one_launch<false>(a); }
-
-// Sets the arrival counter to 0 (a device's first one-launch encode).
-__global__ void clear_word_kernel(uint32_t* w) { *w = 0; }
 
 // ---------------------------------------------------------- decode kernels
 struct DecArgs {
@@ -2018,9 +1985,9 @@ int compress_impl(int dtype, int variant, const void* d_in, size_t n_elems, cons
   uint8_t* out = static_cast<uint8_t*>(d_out);
   Workspace w = workspace_of(out, dtype, n, n_codebooks, variant);
   if (static_ws) {
-    w.tile_count = static_ws + kStaticCountAt;
+    w.tile_count = static_ws;
     w.stage = static_ws + kStaticStageAt;
-    w.block_sum = w.super_sum = nullptr;  // one launch: no block sums
+    w.block_sum = w.super_sum = nullptr;  // at most 64 blocks: never read
   }
 
   // header, codebooks and padding: a launch of their own when the stream is
@@ -2085,15 +2052,8 @@ int compress_impl(int dtype, int variant, const void* d_in, size_t n_elems, cons
   e.cb_args = cb_args;
   e.sums_in_place = blocks <= 64;
   e.prep_in = cb_args ? (e.sums_in_place ? 2 : 1) : 0;
-  e.arrivals = static_ws;
   if (cb_args) prep_args(e.prep, 0);
   else memset(&e.prep, 0, sizeof(e.prep));
-  if (static_ws) {  // one launch: the tiles, then the header workgroup
-    if (!cb_args) return SPLITZIP_E_INVALID;  // checked by the caller
-    if (dtype == SPLITZIP_FP8_E5M2) encode_one_launch_e5m2_kernel<<<tiles + 1, kThreads, 0, stream>>>(e);
-    else encode_one_launch_bf16_kernel<<<tiles + 1, kThreads, 0, stream>>>(e);
-    return hipGetLastError() == hipSuccess ? SPLITZIP_OK : SPLITZIP_E_HIP;
-  }
   if (dtype == SPLITZIP_FP8_E5M2) encode_dense_e5m2_kernel<<<tiles, kThreads, 0, stream>>>(e);
   else if (variant == kSentinel) encode_dense_sentinel_kernel<<<tiles, kThreads, 0, stream>>>(e);
   else if (variant == kTop8) encode_dense_top8_kernel<<<tiles, kThreads, 0, stream>>>(e);
@@ -2133,18 +2093,15 @@ constexpr int kMaxDevices = 256;
 std::mutex g_scratch_mu;
 uint32_t* g_scratch[kMaxDevices] = {};
 
-// The current device's scratch address; *fresh is set when this call looked
-// it up (the device's first call).
-int static_scratch(uint32_t** ws, bool* fresh) {
+// The current device's scratch address.
+int static_scratch(uint32_t** ws) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPLITZIP_E_HIP;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
-  *fresh = false;
   if (g_scratch[dev] == nullptr) {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SPLITZIP_E_HIP;
     g_scratch[dev] = static_cast<uint32_t*>(p);
-    *fresh = true;
   }
   *ws = g_scratch[dev];
   return SPLITZIP_OK;
@@ -2157,20 +2114,15 @@ extern "C" {
 int splitzip_compress_static(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks,
                              uint32_t n_codebooks, size_t segment_elems, void* d_out, size_t out_capacity,
                              uint64_t* d_out_bytes, hipStream_t stream) {
-  if (!dtype_valid(dtype) || n_codebooks == 0 || n_codebooks > (uint32_t)kCbPerPrep) return SPLITZIP_E_INVALID;
+  if (!dtype_valid(dtype)) return SPLITZIP_E_INVALID;
   const uint64_t tile = dtype == SPLITZIP_BF16 ? kEncTileBf16 : kEncTileE5m2;
   if (n_elems > kStaticMaxTiles * tile) return SPLITZIP_E_TOO_LARGE;
   if (n_elems == 0)  // header only: no workspace
     return compress_impl(dtype, kMain, d_in, 0, h_codebooks, n_codebooks, segment_elems, d_out, out_capacity,
                          d_out_bytes, stream);
   uint32_t* ws = nullptr;
-  bool fresh = false;
-  int rc = static_scratch(&ws, &fresh);
+  const int rc = static_scratch(&ws);
   if (rc != SPLITZIP_OK) return rc;
-  if (fresh) {  // the counter must start at 0 (it does at load; this makes sure)
-    clear_word_kernel<<<1, 1, 0, stream>>>(ws);
-    if (hipGetLastError() != hipSuccess) return SPLITZIP_E_HIP;
-  }
   return compress_impl(dtype, kMain, d_in, n_elems, h_codebooks, n_codebooks, segment_elems, d_out, out_capacity,
                        d_out_bytes, stream, ws);
 }
@@ -2242,7 +2194,7 @@ const char* splitzip_status_string(int status) {
     case SPLITZIP_E_CODEBOOK: return "invalid codebook";
     case SPLITZIP_E_CORRUPT: return "corrupt stream";
     case SPLITZIP_E_HIP: return "HIP launch failure";
-    case SPLITZIP_E_TOO_LARGE: return "input larger than the one-launch encoder's workspace";
+    case SPLITZIP_E_TOO_LARGE: return "input larger than splitzip_compress_static's workspace";
     default: return "unknown status";
   }
 }

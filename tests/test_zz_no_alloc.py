@@ -2,9 +2,9 @@
 (its workspace is the library's own device array): called through the C ABI,
 its stream equals splitzip_compress's byte for byte, on two calls in a row
 (the second with a smaller input), at the size limit, with escape-heavy tiles
-(placed by re-encoding), several codebooks, the exact minimum capacity, an
-empty input, and replayed from a HIP graph.  Sizes beyond its limit are
-refused before any GPU work."""
+(placed by re-encoding), several and many codebooks, the exact minimum
+capacity, an empty input, and replayed from a HIP graph.  Sizes beyond its
+limit are refused before any GPU work."""
 import numpy as np
 import pytest
 import torch
@@ -81,17 +81,19 @@ def test_two_calls_in_a_row_second_smaller_e5m2():
 
 
 def test_size_limit():
-    x = kvsynth.random_bits(1024 * 8192, kvsynth.BF16, seed=3, device=DEV)  # exactly 1024 tiles
+    x = kvsynth.random_bits(2048 * 8192, kvsynth.BF16, seed=3, device=DEV)  # exactly 2048 tiles
     cb = O.calibrate(O.BF16, kvsynth.to_numpy_bits(x[:100_000]))
-    _check(x, cb, 0, "1024 tiles")
-    big = kvsynth.random_bits(1024 * 8192 + 1, kvsynth.BF16, seed=4, device=DEV)
+    _check(x, cb, 0, "2048 tiles")
+    y = kvsynth.random_bits(2048 * 16384, kvsynth.E5M2, seed=6, device=DEV)  # E5M2: 2048 tiles of 16384
+    _check(y, O.calibrate(O.E5M2, kvsynth.to_numpy_bits(y[:100_000])), 0, "2048 E5M2 tiles")
+    big = kvsynth.random_bits(2048 * 8192 + 1, kvsynth.BF16, seed=4, device=DEV)
     rc, _, _ = _static(big, cb, 0, cap=_min_capacity(O.BF16, big.numel(), 1))
     assert rc == sz.E_TOO_LARGE
 
 
 def test_escape_heavy_tiles_and_capacity():
     # uniform bit patterns: every tile holds far more escapes than its
-    # staging slot, so the last workgroup encodes them again
+    # staging slot, so the placement pass encodes them again
     x = kvsynth.random_bits(600_001, kvsynth.BF16, seed=5, device=DEV, kind="uniform_bits")
     cb = O.calibrate(O.BF16, kvsynth.to_numpy_bits(x[:5000]))
     _check(x, cb, 0, "uniform bits")
@@ -100,6 +102,14 @@ def test_escape_heavy_tiles_and_capacity():
     assert rc == sz.E_CAPACITY
     rc, _, _ = _static(x, cb, 0, cap=cap)
     assert rc == sz.OK
+
+
+def test_many_codebooks():
+    # more codebooks than fit the kernel arguments: the header launches of their own
+    x = kvsynth.random_bits(200 * 65536 + 3, kvsynth.BF16, seed=8, device=DEV, sigma=2.0)
+    rng = np.random.default_rng(8)
+    cbs = np.stack([rng.permutation(256)[:16] for _ in range(201)]).astype(np.uint8)
+    _check(x, cbs, 65536, "201 codebooks")
 
 
 def test_empty_input():
