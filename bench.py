@@ -36,6 +36,82 @@ def source_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def ceiling_lib():
+    """The copy / read ceiling kernels (libszceiling.so, built beside
+    libsplitzip.so)."""
+    import ctypes
+    path = os.path.join(ROOT, "lossless_kv_cache_splitzip_amd", "libszceiling.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} missing: build with `python -m lossless_kv_cache_splitzip_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz_t = ctypes.c_void_p, ctypes.c_size_t
+    lib.szceiling_copy.argtypes = [vp, vp, sz_t, vp]
+    lib.szceiling_copy.restype = ctypes.c_int
+    lib.szceiling_read.argtypes = [vp, sz_t, vp, ctypes.c_uint32, vp]
+    lib.szceiling_read.restype = ctypes.c_int
+    return lib
+
+
+def ceiling_leg(src, stream, reps: int = 20):
+    """Measured ceilings on `src` (a device tensor, the timed workload):
+    the hand-written copy kernel (16 bytes per lane, non-temporal; read +
+    write bytes / time), the read-only kernel (bytes / time) and torch's
+    device-to-device copy (hipMemcpy path), each the median of `reps`
+    event-timed launches after 3 warm-ups."""
+    import numpy as np
+    import torch
+
+    lib = ceiling_lib()
+    b = src.view(torch.uint8)
+    nbytes = b.numel() - b.numel() % 16
+    dst = torch.empty_like(b)
+    hits = torch.zeros(1, dtype=torch.int32, device=b.device)
+    sh = stream.cuda_stream
+
+    def timed(f, moved):
+        for _ in range(3):
+            f()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            f()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([moved / (e0.elapsed_time(e1) / 1e3) / 1e9 for e0, e1 in ev]))
+
+    def copy():
+        assert lib.szceiling_copy(b.data_ptr(), dst.data_ptr(), nbytes, sh) == 0
+
+    def read():
+        assert lib.szceiling_read(b.data_ptr(), nbytes, hits.data_ptr(), 0x9E3779B9, sh) == 0
+
+    res = {"copy_kernel_GBps": timed(copy, 2 * nbytes), "read_kernel_GBps": timed(read, nbytes),
+           "memcpy_d2d_GBps": timed(lambda: dst.copy_(b), 2 * b.numel()), "bytes": int(b.numel())}
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], b[:nbytes])
+    del dst
+    return res
+
+
+def lscpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:  # noqa: BLE001 - fall back to /proc/cpuinfo
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def counter_traffic(kernels, workload: str):
     """HBM bytes per call (summed over the given kernels) from the committed
     rocprofv3 counter summary of this workload, if it was taken on the current
@@ -56,13 +132,13 @@ def counter_traffic(kernels, workload: str):
     return total
 
 
-def cpu_baseline(wl_name: str, budget_s: float, threads: int):
+def cpu_baseline(wl, cbs, budget_s: float, threads: int):
     """The oracle as it stands (single-threaded C), timed on whole layers of
-    the same workload, one after another, until about budget_s seconds of
-    CPU work (at least one layer).  Each layer is compressed with its own
-    codebook and decompressed again.  The same layers are then run again,
-    one layer per thread on `threads` host threads (the oracle's C calls
-    release the GIL), as the chunk-parallel CPU figure."""
+    the timed GPU tensor itself (copied to the host) with the codebooks the
+    GPU used, one layer after another, until about budget_s seconds of CPU
+    work (at least one layer): compress, then decompress.  The same layers
+    are then run again, one layer per thread on `threads` host threads (the
+    oracle's C calls release the GIL), as the chunk-parallel CPU figure."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -70,15 +146,17 @@ def cpu_baseline(wl_name: str, budget_s: float, threads: int):
     import kvsynth
     import oracle
 
-    spec = kvsynth.SPECS[wl_name]
+    spec = wl.spec
     dtype = spec.dtype
+    per_layer = cbs.shape[0] > 1
+    layer_n = spec.layer_elems if per_layer else wl.n
+    n_layers = spec.layers if per_layer else 1
     done = raw = 0
     t_enc = t_dec = 0.0
     layers = []
-    while done < spec.layers and (t_enc + t_dec) < budget_s:
-        x, c = kvsynth.layer(wl_name, done, device="cpu")
-        x = kvsynth.to_numpy_bits(x)
-        cb = oracle.calibrate(dtype, kvsynth.to_numpy_bits(c))
+    while done < n_layers and (t_enc + t_dec) < budget_s:
+        x = kvsynth.to_numpy_bits(wl.data[done * layer_n:(done + 1) * layer_n])
+        cb = cbs[done if per_layer else 0]
         t0 = time.perf_counter()
         s = oracle.compress(dtype, x, cb)
         t1 = time.perf_counter()
@@ -90,13 +168,16 @@ def cpu_baseline(wl_name: str, budget_s: float, threads: int):
         raw += x.nbytes
         done += 1
         layers.append((x, cb))
+    model = lscpu_model()
     serial = {
         "value": raw / (t_enc + t_dec) / 1e9,
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{done} of {spec.layers} layers ({raw / 2**20:.0f} MiB raw) of the same workload, "
-                  f"compress + decompress, one codebook per layer, one thread",
+        "sample": f"{done} of {n_layers} layers ({raw / 2**20:.0f} MiB raw) of the timed workload: the same bytes "
+                  f"as the GPU run (copied from the device tensor) and the same per-layer codebooks, "
+                  f"compress + decompress, one thread",
+        "cpu_model": model,
         "encode_GBps": raw / t_enc / 1e9,
         "decode_GBps": raw / t_dec / 1e9,
     }
@@ -118,6 +199,7 @@ def cpu_baseline(wl_name: str, budget_s: float, threads: int):
         "cores": threads,
         "kind": "oracle",
         "sample": f"the same {done} layers, compress + decompress, one layer per thread on {threads} threads",
+        "cpu_model": model,
     }
     return serial, parallel
 
@@ -137,23 +219,22 @@ def link_leg(wl, cbs, seg, dtype, reps: int = 3):
     group = (16 << 20) // elem
     if seg and seg % group and group % seg:
         group = seg
-    p = sz.Pipeline(dtype, wl.n, cbs, seg, group, 4, device=wl.data.device)
     out = torch.empty_like(wl.data)
     status = torch.zeros(1, dtype=torch.int32, device=wl.data.device)
     res = {}
-    for mode in ("raw", "compressed"):
-        best, sent = float("inf"), 0
-        for r in range(reps + 1):
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            sizes = p.transfer(wl.data, out, compress=(mode == "compressed"), status=status)
-            t1 = time.perf_counter()
-            if r:
-                best = min(best, t1 - t0)
-            sent = int(sizes.sum())
-        assert int(status.item()) == 0 and torch.equal(out.view(torch.uint8), wl.data.view(torch.uint8))
-        res[mode] = (best * 1e3, sent)
-    del p
+    with sz.Pipeline(dtype, wl.n, cbs, seg, group, 4, device=wl.data.device) as p:
+        for mode in ("raw", "compressed"):
+            best, sent, cpu_frac = float("inf"), 0, 0.0
+            for r in range(reps + 1):
+                torch.cuda.synchronize()
+                t0, c0 = time.perf_counter(), time.process_time()
+                sizes = p.transfer(wl.data, out, compress=(mode == "compressed"), status=status)
+                t1, c1 = time.perf_counter(), time.process_time()
+                if r and t1 - t0 < best:
+                    best, cpu_frac = t1 - t0, (c1 - c0) / (t1 - t0)
+                sent = int(sizes.sum())
+            assert int(status.item()) == 0 and torch.equal(out.view(torch.uint8), wl.data.view(torch.uint8))
+            res[mode] = (best * 1e3, sent, cpu_frac)
     # copy engines: the whole tensor to pinned host memory, and a second
     # pinned buffer to the device, concurrently (both link directions)
     src = wl.data.view(torch.uint8)
@@ -172,8 +253,8 @@ def link_leg(wl, cbs, seg, dtype, reps: int = 3):
         if r:
             dma = min(dma, time.perf_counter() - t0)
     del h1, h2, out
-    raw_ms, raw_sent = res["raw"]
-    c_ms, c_sent = res["compressed"]
+    raw_ms, raw_sent, raw_cpu = res["raw"]
+    c_ms, c_sent, c_cpu = res["compressed"]
     return {
         "link": "pinned host memory over PCIe, copy engines both ways",
         "group_elems": group, "depth": 4,
@@ -182,6 +263,8 @@ def link_leg(wl, cbs, seg, dtype, reps: int = 3):
         "raw_GBps": wl.raw_bytes / (raw_ms / 1e3) / 1e9,
         "compressed_GBps": wl.raw_bytes / (c_ms / 1e3) / 1e9,
         "copy_engines_both_ways_ms": dma * 1e3,
+        # host CPU time of the process during the best transfer, per second of it
+        "host_cpu_per_wall_raw": raw_cpu, "host_cpu_per_wall_compressed": c_cpu,
     }
 
 
@@ -295,8 +378,19 @@ def per_layer_graph_leg(reps: int = 50):
         for _ in range(reps):
             sz.decompress(out, wl.n, d, out=y, status=st, in_bytes=cap)
 
+    out_s = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    nb_s = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+    def enc_static():
+        for _ in range(reps):
+            sz.compress_static(wl.data, cbs, out=out_s, out_bytes=nb_s)
+
+    with torch.cuda.stream(side):
+        enc_static()
+    torch.cuda.synchronize()
+    assert torch.equal(out_s[:int(nb_s.item())], eager_stream)
     graphs = {}
-    for name, f in (("enc", enc), ("dec", dec)):
+    for name, f in (("enc", enc), ("dec", dec), ("enc_static", enc_static)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             f()
@@ -315,13 +409,141 @@ def per_layer_graph_leg(reps: int = 50):
 
     res = {"workload": "kv_layer_bf16", "raw_bytes": wl.raw_bytes, "calls": reps,
            "eager_encode_us": per_call_us(enc), "eager_decode_us": per_call_us(dec),
-           "graph_encode_us": per_call_us(graphs["enc"].replay), "graph_decode_us": per_call_us(graphs["dec"].replay)}
+           "graph_encode_us": per_call_us(graphs["enc"].replay), "graph_decode_us": per_call_us(graphs["dec"].replay),
+           # splitzip_compress_static: one launch, workspace in the library's own memory
+           "eager_encode_static_us": per_call_us(enc_static),
+           "graph_encode_static_us": per_call_us(graphs["enc_static"].replay)}
     y.zero_()
+    out_s.zero_()
     graphs["enc"].replay()
     graphs["dec"].replay()
+    graphs["enc_static"].replay()
     torch.cuda.synchronize()
     assert int(st.item()) == 0 and torch.equal(out[:int(nb.item())], eager_stream)
+    assert torch.equal(out_s[:int(nb_s.item())], eager_stream)
     assert torch.equal(y.view(torch.uint8), wl.data.view(torch.uint8))
+    return res
+
+
+WORKLOADS = ["kv_layer_bf16", "llama3_8b_kv_bf16", "long_ctx_heavy_tail_bf16", "edge_const_exponent",
+             "edge_uniform_bits", "edge_special_values", "llama3_70b_kv_e5m2"]
+
+
+def algorithmic_bytes(dtype: int, n: int, n_esc: int) -> int:
+    """Bytes a compress (or decompress) call must move: the raw values, the
+    codes, the sign|mantissa section and 3 bytes per escape."""
+    import kvsynth
+    raw = n * (2 if dtype == kvsynth.BF16 else 1)
+    dense = (n + 1) // 2 + (n if dtype == kvsynth.BF16 else 3 * ((n + 7) // 8))
+    return raw + dense + 3 * n_esc
+
+
+def make_evict(dev, stream):
+    """Before a cold call: 512 MiB written, then a separate 768 MiB read (the
+    memory-side cache holds 256 MB), so the timed call finds neither its own
+    data cached nor dirty lines of the eviction left to write back."""
+    import torch
+    lib = ceiling_lib()
+    w = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    r = torch.zeros(768 << 20, dtype=torch.uint8, device=dev)
+    hits = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def evict(i: int):
+        w.fill_(i & 0xFF)
+        assert lib.szceiling_read(r.data_ptr(), r.numel(), hits.data_ptr(), 0x9E3779B9, stream.cuda_stream) == 0
+
+    return evict
+
+
+def warm_up(fs, min_s: float = 0.2):
+    """Runs the calls in `fs` in turn for at least min_s seconds (and three
+    rounds): the GPU's clocks ramp up under load after an idle spell."""
+    import time as _t
+    import torch
+    t0 = _t.perf_counter()
+    r = 0
+    while r < 3 or _t.perf_counter() - t0 < min_s:
+        for f in fs:
+            f()
+        torch.cuda.synchronize()
+        r += 1
+
+
+def timed_calls_ms(f, stream, reps: int, evict=None):
+    """Mean event time (ms) of `reps` calls of f on `stream`; with `evict`,
+    the caches are flushed of f's data before each call, outside the timed
+    interval."""
+    import numpy as np
+    import torch
+    ev = []
+    for i in range(reps):
+        if evict is not None:
+            evict(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        f()
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def workload_leg(name, dev, stream, evict, reps: int = 10, prebuilt=None):
+    """One workload at full size: warm (back-to-back calls) and cold (the
+    memory-side cache evicted before each call) event-timed compress and
+    decompress, the copy-kernel ceiling on its input, ratio, escape rate,
+    algorithmic bytes and roofline fractions.  The round trip is checked."""
+    import numpy as np
+    import torch
+
+    import kvsynth
+    import lossless_kv_cache_splitzip_amd as sz
+
+    if prebuilt is None:
+        wl = kvsynth.make(name, device=dev)
+        cbs = np.stack([sz.splitzip_calibrate(wl.spec.dtype, kvsynth.to_numpy_bits(c)) for c in wl.calib])
+    else:
+        wl, cbs = prebuilt
+    d = wl.spec.dtype
+    seg = wl.segment_elems if cbs.shape[0] > 1 else 0
+    cap = sz.splitzip_max_compressed_size(d, wl.n, cbs.shape[0])
+    out = torch.empty(cap, dtype=torch.uint8, device=dev)
+    nb = torch.zeros(1, dtype=torch.int64, device=dev)
+    y = torch.empty_like(wl.data)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def enc():
+        sz.compress(wl.data, cbs, seg, out=out, out_bytes=nb, stream=stream)
+
+    def dec():
+        sz.decompress(out, wl.n, d, out=y, status=st, in_bytes=cap, stream=stream)
+
+    enc()
+    dec()
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and torch.equal(y.view(torch.uint8), wl.data.view(torch.uint8)), name
+    S = int(nb.item())
+    E = int(np.frombuffer(out[16:24].cpu().numpy().tobytes(), "<u8")[0])
+    warm_up([enc, dec])
+    t = {"encode_ms": timed_calls_ms(enc, stream, reps), "decode_ms": timed_calls_ms(dec, stream, reps),
+         "encode_cold_ms": timed_calls_ms(enc, stream, reps, evict),
+         "decode_cold_ms": timed_calls_ms(dec, stream, reps, evict)}
+    ceil = ceiling_leg(wl.data, stream, reps=10)
+    alg = algorithmic_bytes(d, wl.n, E)
+    raw = wl.raw_bytes
+    res = {"element_type": "bf16" if d == kvsynth.BF16 else "fp8_e5m2", "elements": wl.n, "raw_bytes": raw,
+           "codebooks": int(cbs.shape[0]), "compression_ratio": raw / S, "escape_rate": E / wl.n,
+           "algorithmic_bytes": alg, "copy_kernel_GBps": ceil["copy_kernel_GBps"]}
+    for k, ms in t.items():
+        what = k.replace("_ms", "")
+        res[k] = ms
+        res[what + "_GBps"] = raw / (ms / 1e3) / 1e9                     # raw bytes per second
+        res[what + "_frac_of_8TBps"] = alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS  # algorithmic bytes
+        res[what + "_frac_of_copy_kernel"] = alg / (ms / 1e3) / 1e9 / ceil["copy_kernel_GBps"]
+    del out, y, nb, st
+    if prebuilt is None:
+        del wl
+    torch.cuda.empty_cache()
     return res
 
 
@@ -342,11 +564,17 @@ def main():
     ap.add_argument("--no-link", action="store_true", help="skip the pipelined host-link transfer leg")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the one-layer graph leg (its calls launch the same kernels on a 4 MiB input)")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload map")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="only the timed steps and the copy ceiling (for rocprofv3 runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this codec benchmark runs on one GPU; multi-GPU runs are not part of it",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.profile_run:
+        args.no_link = args.no_layer = args.no_workloads = True
+        args.cpu_budget = 0
 
     import numpy as np
     import torch
@@ -406,26 +634,16 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, encode {enc_ms:.3f} ms, decode {dec_ms:.3f} ms")
 
-    # measured device-to-device copy ceiling (hipMemcpyAsync of the input,
-    # read + write bytes / time): median of 20 copies
-    cp_src = wl.data.view(torch.uint8)
-    cp_dst = torch.empty_like(cp_src)
-    for _ in range(3):
-        cp_dst.copy_(cp_src)
-    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-    for c0, c1 in cev:
-        c0.record(stream)
-        cp_dst.copy_(cp_src)
-        c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = float(np.median([2 * cp_src.numel() / (c0.elapsed_time(c1) / 1e3) / 1e9 for c0, c1 in cev]))
-    del cp_dst
+    # measured ceilings on the same input: hand-written copy and read kernels,
+    # and torch's device-to-device copy
+    ceil = ceiling_leg(wl.data, stream)
+    copy_gbps = ceil["copy_kernel_GBps"]
+    log(f"[bench] copy kernel {copy_gbps:.0f} GB/s, read kernel {ceil['read_kernel_GBps']:.0f} GB/s, "
+        f"torch copy {ceil['memcpy_d2d_GBps']:.0f} GB/s")
 
-    dense_out = (n + 1) // 2 + (n if dtype == kvsynth.BF16 else 3 * ((n + 7) // 8))
-    alg_enc = raw + dense_out + 3 * n_esc          # read input, write codes + sign|mantissa + escapes
-    alg_dec = dense_out + 3 * n_esc + raw          # read codes + sign|mantissa + escapes, write values
-    enc_gbps = alg_enc / (enc_ms / 1e3) / 1e9
-    dec_gbps = alg_dec / (dec_ms / 1e3) / 1e9
+    alg = algorithmic_bytes(dtype, n, n_esc)   # same for encode (read raw, write stream) and decode
+    enc_gbps = alg / (enc_ms / 1e3) / 1e9
+    dec_gbps = alg / (dec_ms / 1e3) / 1e9
     sfx = "bf16" if dtype == kvsynth.BF16 else "e5m2"
     # the launches of one compress call: a prep launch only for more than 128
     # codebooks (else the header work rides in another launch), the block
@@ -434,23 +652,43 @@ def main():
     enc_kernels = (["prep_kernel"] if cbs.shape[0] > 128 else []) + [f"encode_dense_{sfx}_kernel"] + \
         (["encode_sums_kernel"] if -(-tiles // 64) > 64 else []) + [f"encode_place_{sfx}_kernel"]
     dname = f"decode_{sfx}_kernel"
-    abl = ablation_leg(wl, cbs, seg, stream, enc_ms, dec_ms) if dtype == kvsynth.BF16 else None
-    if abl:
-        for k, r in abl.items():
-            log(f"[bench] {k}: ratio {r['compression_ratio']:.4f}, escapes {100 * r['escape_rate']:.2f}%, "
-                f"decode {r['decode_ms']:.3f} ms ({r['decode_slowdown_vs_top16']:.2f}x top-16)")
-    calib = calibrate_leg(wl, seg, cbs, stream)
-    log(f"[bench] device calibration of {calib['codebooks']} codebooks: {calib['ms']:.3f} ms "
-        f"({calib['GBps']:.0f} GB/s)")
-    link = None if args.no_link else link_leg(wl, cbs, seg, dtype)
-    if link:
+
+    workloads = None
+    if not args.no_workloads:
+        evict = make_evict(dev, stream)
+        workloads = {}
+        for name in WORKLOADS:
+            log(f"[bench] workload {name}")
+            workloads[name] = workload_leg(name, dev, stream, evict,
+                                           prebuilt=(wl, cbs) if name == args.workload else None)
+            r = workloads[name]
+            log(f"[bench]   ratio {r['compression_ratio']:.4f} escapes {100 * r['escape_rate']:.2f}% "
+                f"encode {r['encode_GBps']:.0f} GB/s ({r['encode_frac_of_8TBps']:.3f}; cold "
+                f"{r['encode_cold_frac_of_8TBps']:.3f}) decode {r['decode_GBps']:.0f} GB/s "
+                f"({r['decode_frac_of_8TBps']:.3f}; cold {r['decode_cold_frac_of_8TBps']:.3f})")
+        del evict
+        torch.cuda.empty_cache()
+    abl = calib = link = layer = None
+    if not args.profile_run:
+        abl = ablation_leg(wl, cbs, seg, stream, enc_ms, dec_ms) if dtype == kvsynth.BF16 else None
+        if abl:
+            for k, r in abl.items():
+                log(f"[bench] {k}: ratio {r['compression_ratio']:.4f}, escapes {100 * r['escape_rate']:.2f}%, "
+                    f"decode {r['decode_ms']:.3f} ms ({r['decode_slowdown_vs_top16']:.2f}x top-16)")
+        calib = calibrate_leg(wl, seg, cbs, stream)
+        log(f"[bench] device calibration of {calib['codebooks']} codebooks: {calib['ms']:.3f} ms "
+            f"({calib['GBps']:.0f} GB/s)")
+    if not args.no_link:
+        link = link_leg(wl, cbs, seg, dtype)
         log(f"[bench] link: raw {link['raw_ms']:.2f} ms, compressed {link['compressed_ms']:.2f} ms, "
-            f"speedup {link['speedup']:.3f}")
-    layer = None if args.no_layer else per_layer_graph_leg()
-    if layer:
+            f"speedup {link['speedup']:.3f}, host CPU {link['host_cpu_per_wall_compressed']:.2f} s per s")
+    if not args.no_layer:
+        layer = per_layer_graph_leg()
         log(f"[bench] one-layer calls: eager {layer['eager_encode_us']:.1f} / {layer['eager_decode_us']:.1f} us, "
-            f"graph-replayed {layer['graph_encode_us']:.1f} / {layer['graph_decode_us']:.1f} us (encode / decode)")
-    cpu, cpu_par = cpu_baseline(args.workload, args.cpu_budget, args.cpu_threads) if args.cpu_budget > 0 else (None, None)
+            f"graph-replayed {layer['graph_encode_us']:.1f} / {layer['graph_decode_us']:.1f} us (encode / decode); "
+            f"one-launch encode eager {layer['eager_encode_static_us']:.1f} us, "
+            f"graph-replayed {layer['graph_encode_static_us']:.1f} us")
+    cpu, cpu_par = cpu_baseline(wl, cbs, args.cpu_budget, args.cpu_threads) if args.cpu_budget > 0 else (None, None)
 
     line = {
         "metric": "encode & decode GB/s of raw BF16 KV, compression ratio, % of HBM roofline",
@@ -475,18 +713,23 @@ def main():
         "decode_ms": dec_ms,
         "compression_ratio": raw / stream_bytes,
         "escape_rate": n_esc / n,
-        "memcpy_d2d_GBps": copy_gbps,
+        "copy_kernel_GBps": copy_gbps,
+        "read_kernel_GBps": ceil["read_kernel_GBps"],
+        "memcpy_d2d_GBps": ceil["memcpy_d2d_GBps"],
         # the longest single kernel of a step; a decompress call is exactly one
         # launch of it, so the event interval is its duration
         "roofline": {"bound": "hbm", "kernel": dname, "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dec_gbps / HBM_PEAK_GBPS, "frac_of_memcpy": dec_gbps / copy_gbps,
-                     "traffic": counter_traffic([dname], args.workload), "algorithmic_bytes": alg_dec},
+                     "frac": dec_gbps / HBM_PEAK_GBPS, "frac_of_copy_kernel": dec_gbps / copy_gbps,
+                     "frac_of_memcpy": dec_gbps / ceil["memcpy_d2d_GBps"],
+                     "traffic": counter_traffic([dname], args.workload), "algorithmic_bytes": alg},
         # a compress call: the launches listed in "kernel"
         "roofline_encode": {"bound": "hbm", "kernel": "+".join(enc_kernels), "achieved": enc_gbps,
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": enc_gbps / HBM_PEAK_GBPS,
-                            "frac_of_memcpy": enc_gbps / copy_gbps,
-                            "traffic": counter_traffic(enc_kernels, args.workload), "algorithmic_bytes": alg_enc},
+                            "frac_of_copy_kernel": enc_gbps / copy_gbps,
+                            "frac_of_memcpy": enc_gbps / ceil["memcpy_d2d_GBps"],
+                            "traffic": counter_traffic(enc_kernels, args.workload), "algorithmic_bytes": alg},
         "cpu_baseline": cpu,
+        "workloads": workloads,
         "link_transfer": link,
         "calibrate_device": calib,
         "ablations": abl,

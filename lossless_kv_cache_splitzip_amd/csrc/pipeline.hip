@@ -14,11 +14,11 @@
 // waits on another (cross-stream event waits cost up to a millisecond each
 // between copy-engine queues on this system).  When no step can be queued,
 // the thread polls for a short while (the next step is often moments away)
-// and then sleeps in the HIP runtime on the oldest outstanding step's event
-// (blocking-sync events), so it does not hold a host core for the whole
-// transfer.  A compressed group's size exists only on the device: the
-// encoder writes it into the pinned link buffer, where the host reads it
-// before queuing the group's copies.
+// and then naps between polls, so it does not hold a host core for the
+// whole transfer (waiting in hipEventSynchronize, even on blocking-sync
+// events, kept a core busy).  A compressed group's size exists only on the
+// device: the encoder writes it into the pinned link buffer, where the host
+// reads it before queuing the group's copies.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -113,15 +113,9 @@ int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, cons
   Events ev;
   ev.e.assign(4 * (size_t)depth, nullptr);
   for (hipEvent_t& x : ev.e)
-    if (hipEventCreateWithFlags(&x, hipEventDisableTiming | hipEventBlockingSync) != hipSuccess)
-      return SPLITZIP_E_HIP;
-  std::vector<uint64_t> seq(4 * (size_t)depth, 0);  // order in which the events were recorded
-  uint64_t recorded = 0;
+    if (hipEventCreateWithFlags(&x, hipEventDisableTiming) != hipSuccess) return SPLITZIP_E_HIP;
   auto E = [&](int kind, uint64_t g) { return ev.e[4 * (g % depth) + kind]; };
-  auto record = [&](int kind, uint64_t g, hipStream_t st) {
-    seq[4 * (g % depth) + kind] = ++recorded;
-    return hipEventRecord(E(kind, g), st) == hipSuccess;
-  };
+  auto record = [&](int kind, uint64_t g, hipStream_t st) { return hipEventRecord(E(kind, g), st) == hipSuccess; };
   hipError_t qerr = hipSuccess;
   auto done = [&](int kind, uint64_t g) {  // step `kind` of group g has completed
     const hipError_t q = hipEventQuery(E(kind, g));
@@ -147,28 +141,13 @@ int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, cons
   // next group to take each step: compress, copy out, copy back, decode
   uint64_t nc = 0, nd = 0, nh = 0, nx = 0;
   const uint64_t G = p.groups;
-  // after a step was queued, poll this long before sleeping on an event
+  // after a step was queued, poll this long before napping between polls
   constexpr auto kPoll = std::chrono::microseconds(40);
+  constexpr auto kNap = std::chrono::microseconds(20);
+  // a step that makes no progress for this long means the device stopped
+  // answering: give up rather than wait forever
+  constexpr auto kStall = std::chrono::seconds(60);
   auto last_progress = std::chrono::steady_clock::now();
-  // The oldest recorded event, among those the queue conditions below wait
-  // for, that has not completed: waiting on it never waits on work that
-  // was not queued.  -1 if there is none.
-  auto oldest_pending = [&]() -> int {
-    int best = -1;
-    auto consider = [&](int kind, uint64_t g, bool recorded_already) {
-      if (!recorded_already) return;
-      const int i = 4 * (int)(g % depth) + kind;
-      if (best >= 0 && seq[i] >= seq[best]) return;
-      if (!done(kind, g)) best = i;
-    };
-    if (nc < G && nc >= depth) consider(1, nc - depth, nd > nc - depth);
-    if (nd < nc) consider(0, nd, true);
-    if (nd < nc && nd >= depth) consider(2, nd - depth, nh > nd - depth);
-    if (nh < nd) consider(1, nh, true);
-    if (compress && nh < nd && nh >= depth) consider(3, nh - depth, nx > nh - depth);
-    if (compress && nx < nh) consider(2, nx, true);
-    return best;
-  };
   while (compress ? nx < G : nh < G) {
     bool progress = false;
     // compress g: its send slot is free once group g - depth was copied out
@@ -227,14 +206,11 @@ int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, cons
     if (qerr != hipSuccess) return SPLITZIP_E_HIP;
     if (progress) {
       last_progress = std::chrono::steady_clock::now();
-    } else if (std::chrono::steady_clock::now() - last_progress < kPoll) {
-      std::this_thread::yield();
     } else {
-      const int i = oldest_pending();
-      if (qerr != hipSuccess) return SPLITZIP_E_HIP;
-      // none pending: a condition just turned true, the next pass queues it
-      if (i >= 0 && hipEventSynchronize(ev.e[i]) != hipSuccess) return SPLITZIP_E_HIP;
-      last_progress = std::chrono::steady_clock::now();
+      const auto idle = std::chrono::steady_clock::now() - last_progress;
+      if (idle > kStall) return SPLITZIP_E_HIP;
+      if (idle < kPoll) std::this_thread::yield();
+      else std::this_thread::sleep_for(kNap);
     }
   }
   for (int i = 0; i < 4; ++i)
