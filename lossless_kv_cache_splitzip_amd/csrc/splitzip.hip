@@ -115,18 +115,30 @@ struct Workspace {
   uint64_t end;  // bytes from the stream start
 };
 
-__host__ inline Workspace workspace_of(uint8_t* out, int dtype, uint64_t n, uint64_t k, int variant = kMain) {
+// Byte offsets of the workspace parts from the stream start.
+struct WorkspaceLayout {
+  uint64_t block_sum, super_sum, tile_count, stage, end;
+};
+
+__host__ inline WorkspaceLayout workspace_layout(int dtype, uint64_t n, uint64_t k, int variant = kMain) {
   const uint64_t tiles = divup(n, 8192), blocks = divup(tiles, 64);
+  WorkspaceLayout l;
+  l.block_sum = workspace_offset(dtype, n, k, variant);
+  l.super_sum = l.block_sum + 8 * blocks;
+  l.tile_count = round256(l.block_sum + 8 * (blocks + divup(blocks, 64)));  // 16-byte loads in encode_sums
+  l.stage = round256(l.tile_count + 4 * tiles);
+  l.end = round256(l.stage + 4ull * stage_slot(variant) * tiles);
+  return l;
+}
+
+__host__ inline Workspace workspace_of(uint8_t* out, int dtype, uint64_t n, uint64_t k, int variant = kMain) {
+  const WorkspaceLayout l = workspace_layout(dtype, n, k, variant);
   Workspace w;
-  uint64_t at = workspace_offset(dtype, n, k, variant);
-  w.block_sum = reinterpret_cast<uint64_t*>(out + at);
-  w.super_sum = w.block_sum + blocks;
-  at = round256(at + 8 * (blocks + divup(blocks, 64)));
-  w.tile_count = reinterpret_cast<uint32_t*>(out + at);  // 16-byte loads in encode_sums
-  at = round256(at + 4 * tiles);
-  w.stage = reinterpret_cast<uint32_t*>(out + at);
-  at += 4ull * stage_slot(variant) * tiles;
-  w.end = round256(at);
+  w.block_sum = reinterpret_cast<uint64_t*>(out + l.block_sum);
+  w.super_sum = reinterpret_cast<uint64_t*>(out + l.super_sum);
+  w.tile_count = reinterpret_cast<uint32_t*>(out + l.tile_count);
+  w.stage = reinterpret_cast<uint32_t*>(out + l.stage);
+  w.end = l.end;
   return w;
 }
 
@@ -1931,7 +1943,7 @@ int codebooks_valid(int dtype, const uint8_t* cbs, uint32_t k) {
 // Worst-case stream plus encoder workspace.
 size_t max_size_of(int dtype, int variant, size_t n_elems, uint32_t n_codebooks) {
   if (!dtype_valid(dtype) || n_codebooks == 0 || n_codebooks > kMaxK || n_elems > kMaxN) return 0;
-  return workspace_of(nullptr, dtype, n_elems, n_codebooks, variant).end;
+  return workspace_layout(dtype, n_elems, n_codebooks, variant).end;
 }
 
 }  // namespace

@@ -73,6 +73,12 @@ def test_argument_errors_return_before_any_gpu_work():
     assert sz.splitzip_compress(O.BF16, fake, 200000, two, 2, 65536, fake, 1 << 30, None, None) == sz.E_INVALID
     assert sz.splitzip_compress(O.BF16, fake, 100, two, 2, 1000, fake, 1 << 30, None, None) == sz.E_INVALID
     assert sz.splitzip_decompress(fake, 63, O.BF16, 10, fake, None, None) == sz.E_INVALID
+    # the static-scratch encoder refuses a bad dtype and inputs beyond its limit first
+    assert sz.splitzip_compress_static(3, fake, 10, cb, 1, 0, fake, 1 << 30, None, None) == sz.E_INVALID
+    assert sz.splitzip_compress_static(O.BF16, fake, 2048 * 8192 + 1, cb, 1, 0, fake, 1 << 40, None,
+                                       None) == sz.E_TOO_LARGE
+    assert sz.splitzip_compress_static(O.E5M2, fake, 2048 * 16384 + 1, cb, 1, 0, fake, 1 << 40, None,
+                                       None) == sz.E_TOO_LARGE
     assert sz.splitzip_decompress(fake, 1000, 7, 10, fake, None, None) == sz.E_INVALID
     assert sz.splitzip_decompress(fake, 1000, O.BF16, 10, fake + 8, None, None) == sz.E_INVALID
     assert sz.status_string(sz.E_CORRUPT) == "corrupt stream"
