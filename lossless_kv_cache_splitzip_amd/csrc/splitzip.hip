@@ -376,6 +376,7 @@ struct TileEsc {
   uint32_t agg;      // escapes in the tile
   uint32_t rank[4];  // per group (4 groups: BF16 8 elements per thread, E5M2 16)
   uint32_t mask[4];  // escaped elements of each group, bit j = element j
+  uint32_t g01, g23; // escapes of groups 0 and 1, 2 and 3 (16-bit fields; the same in every thread)
 };
 
 __device__ inline void wave_totals_to_lds(EncShared& sh, uint32_t i01, uint32_t i23, uint32_t tid) {
@@ -406,6 +407,8 @@ __device__ inline void tile_ranks4(EncShared& sh, const uint32_t cnt[4], TileEsc
   }
   const uint32_t g0 = tot01 & 0xFFFF, g1 = tot01 >> 16, g2 = tot23 & 0xFFFF, g3 = tot23 >> 16;
   r.agg = g0 + g1 + g2 + g3;
+  r.g01 = tot01;
+  r.g23 = tot23;
   const uint32_t x01 = pre01 + i01 - p01, x23 = pre23 + i23 - p23;
   r.rank[0] = x01 & 0xFFFF;
   r.rank[1] = g0 + (x01 >> 16);
@@ -584,22 +587,30 @@ __device__ inline bool ranks_miss(uint32_t k, uint32_t count, uint32_t w0, uint3
   return k + count <= w0 || (k >= w0 && k - w0 >= wlen);
 }
 
+// Words of group g of a tile's registers, by selects (no scratch memory).
+__device__ inline uint4 pick_group(const TileIn& in, uint32_t g) {
+  return make_uint4(pick4(in.w[0].x, in.w[1].x, in.w[2].x, in.w[3].x, g), pick4(in.w[0].y, in.w[1].y, in.w[2].y, in.w[3].y, g),
+                    pick4(in.w[0].z, in.w[1].z, in.w[2].z, in.w[3].z, g), pick4(in.w[0].w, in.w[1].w, in.w[2].w, in.w[3].w, g));
+}
+
+// The records of group g of an escape-dense BF16 tile, handed to
+// put(index within the group, position, exponent): each element of the
+// thread is tried in turn (unrolled, so its word is a fixed register) and,
+// if escaped, put at its rank in the group; no per-escape loop.
 template <typename Put>
-__device__ inline void window_escapes_bf16(uint64_t tile, const TileEsc& r, const TileIn& in, uint32_t w0,
-                                           uint32_t wlen, uint32_t tid, Put put) {
+__device__ inline void group_escapes_bf16(uint64_t tile, const TileEsc& r, const TileIn& in, uint32_t g,
+                                          uint32_t g_first, uint32_t tid, Put put) {
   const uint32_t in_chunk = (uint32_t)(tile & 7) * (uint32_t)kEncTileBf16;
+  const uint32_t f = pick4(r.mask[0], r.mask[1], r.mask[2], r.mask[3], g);
+  if (!f) return;
+  const uint32_t m = flag_mask4(f << 4) | (flag_mask4(f << 3) << 4);  // element j at bit j
+  const uint32_t k0 = pick4(r.rank[0], r.rank[1], r.rank[2], r.rank[3], g) - g_first;
+  const uint4 w = pick_group(in, g);
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  const uint32_t p0 = in_chunk + g * 2048 + 8 * tid;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const uint32_t f = r.mask[g];
-    uint32_t m = f ? flag_mask4(f << 4) | (flag_mask4(f << 3) << 4) : 0u;
-    uint32_t k = r.rank[g];
-    if (ranks_miss(k, __builtin_popcount(m), w0, wlen)) continue;
-    while (m) {
-      const uint32_t j = __builtin_ctz(m);
-      m &= m - 1;
-      const uint32_t x = pick4(in.w[g].x, in.w[g].y, in.w[g].z, in.w[g].w, j >> 1) >> (16 * (j & 1));
-      put(k++, in_chunk + g * 2048 + 8 * tid + j, (x >> 7) & 0xFF);
-    }
+  for (uint32_t j = 0; j < 8; ++j) {
+    if ((m >> j) & 1u) put(k0 + __builtin_popcount(m & ((1u << j) - 1u)), p0 + j, (wd[j >> 1] >> (16 * (j & 1) + 7)) & 0xFF);
   }
 }
 
@@ -760,16 +771,17 @@ template <typename Put>
 __device__ inline void window_escapes_e5m2(uint64_t tile, const TileEsc& r, const TileIn& in, uint32_t w0,
                                            uint32_t wlen, uint32_t tid, Put put) {
   const uint32_t in_chunk = (uint32_t)(tile & 3) * (uint32_t)kEncTileE5m2;
+#pragma unroll 1
+  for (uint32_t g = 0; g < 4; ++g) {
+    const uint32_t m = pick4(r.mask[0], r.mask[1], r.mask[2], r.mask[3], g);  // element j at bit j
+    const uint32_t k0 = pick4(r.rank[0], r.rank[1], r.rank[2], r.rank[3], g);
+    if (ranks_miss(k0, __builtin_popcount(m), w0, wlen)) continue;
+    const uint4 w = pick_group(in, g);
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t p0 = in_chunk + g * 4096 + 16 * tid;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    uint32_t m = r.mask[g];
-    uint32_t k = r.rank[g];
-    if (ranks_miss(k, __builtin_popcount(m), w0, wlen)) continue;
-    while (m) {
-      const uint32_t j = __builtin_ctz(m);
-      m &= m - 1;
-      const uint32_t x = pick4(in.w[g].x, in.w[g].y, in.w[g].z, in.w[g].w, j >> 2) >> (8 * (j & 3));
-      put(k++, in_chunk + g * 4096 + 16 * tid + j, (x >> 2) & 0x1F);
+    for (uint32_t j = 0; j < 16; ++j) {
+      if ((m >> j) & 1u) put(k0 + __builtin_popcount(m & ((1u << j) - 1u)), p0 + j, (wd[j >> 2] >> (8 * (j & 3) + 2)) & 0x1F);
     }
   }
 }
@@ -1050,15 +1062,31 @@ __device__ void place_range(const EncArgs& a, PlaceLds<kMax>& sh, EncShared& esh
     }
     const TileEsc r = kBf16 ? encode_tile_bf16<kVariant>(a, esh, tt, in, false, tid_i)
                             : encode_tile_e5m2(a, esh, tt, in, false, tid_i);
-    for (uint32_t w0 = 0; w0 < n_i; w0 += kPlaceRecs) {  // BF16: one window per 2048 records
-      auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) {
-        if (k - w0 < kPlaceRecs) sh.rec[k - w0] = pos | (val << 16);
-      };
-      if (kBf16) window_escapes_bf16(tt, r, in, w0, kPlaceRecs, tid_i, stage);
-      else window_escapes_e5m2(tt, r, in, w0, kPlaceRecs, tid_i, stage);
-      __syncthreads();
-      write_records<kVariant>(a, sh.rec, base + sh.pre_all[i] + w0, std::min<uint32_t>(kPlaceRecs, n_i - w0), tid_i);
-      __syncthreads();  // sh.rec and esh are reused
+    if (kBf16) {
+      // one window per group: a group of 2048 elements holds at most
+      // kPlaceRecs records, and its records follow the lower groups'
+#pragma unroll 1
+      for (uint32_t g = 0, g_first = 0; g < 4; ++g) {
+        const uint32_t cnt = ((g < 2 ? r.g01 : r.g23) >> (16 * (g & 1))) & 0xFFFFu;  // the same in every thread
+        if (cnt) {
+          group_escapes_bf16(tt, r, in, g, g_first, tid_i,
+                             [&](uint32_t k, uint32_t pos, uint32_t val) { sh.rec[k] = pos | (val << 16); });
+          __syncthreads();
+          write_records<kVariant>(a, sh.rec, base + sh.pre_all[i] + g_first, cnt, tid_i);
+          __syncthreads();  // sh.rec is reused
+        }
+        g_first += cnt;
+      }
+    } else {
+      for (uint32_t w0 = 0; w0 < n_i; w0 += kPlaceRecs) {  // one window per 2048 records
+        auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) {
+          if (k - w0 < kPlaceRecs) sh.rec[k - w0] = pos | (val << 16);
+        };
+        window_escapes_e5m2(tt, r, in, w0, kPlaceRecs, tid_i, stage);
+        __syncthreads();
+        write_records<kVariant>(a, sh.rec, base + sh.pre_all[i] + w0, std::min<uint32_t>(kPlaceRecs, n_i - w0), tid_i);
+        __syncthreads();  // sh.rec and esh are reused
+      }
     }
   }
 }
