@@ -653,6 +653,11 @@ def main():
         (["encode_sums_kernel"] if -(-tiles // 64) > 64 else []) + [f"encode_place_{sfx}_kernel"]
     dname = f"decode_{sfx}_kernel"
 
+    # the host-link leg first: host copies measured slower after the legs below
+    link = None if args.no_link else link_leg(wl, cbs, seg, dtype)
+    if link:
+        log(f"[bench] link: raw {link['raw_ms']:.2f} ms, compressed {link['compressed_ms']:.2f} ms, "
+            f"speedup {link['speedup']:.3f}, host CPU {link['host_cpu_per_wall_compressed']:.2f} s per s")
     workloads = None
     if not args.no_workloads:
         evict = make_evict(dev, stream)
@@ -668,7 +673,7 @@ def main():
                 f"({r['decode_frac_of_8TBps']:.3f}; cold {r['decode_cold_frac_of_8TBps']:.3f})")
         del evict
         torch.cuda.empty_cache()
-    abl = calib = link = layer = None
+    abl = calib = layer = None
     if not args.profile_run:
         abl = ablation_leg(wl, cbs, seg, stream, enc_ms, dec_ms) if dtype == kvsynth.BF16 else None
         if abl:
@@ -678,10 +683,6 @@ def main():
         calib = calibrate_leg(wl, seg, cbs, stream)
         log(f"[bench] device calibration of {calib['codebooks']} codebooks: {calib['ms']:.3f} ms "
             f"({calib['GBps']:.0f} GB/s)")
-    if not args.no_link:
-        link = link_leg(wl, cbs, seg, dtype)
-        log(f"[bench] link: raw {link['raw_ms']:.2f} ms, compressed {link['compressed_ms']:.2f} ms, "
-            f"speedup {link['speedup']:.3f}, host CPU {link['host_cpu_per_wall_compressed']:.2f} s per s")
     if not args.no_layer:
         layer = per_layer_graph_leg()
         log(f"[bench] one-layer calls: eager {layer['eager_encode_us']:.1f} / {layer['eager_decode_us']:.1f} us, "
