@@ -150,11 +150,15 @@ const char* splitzip_status_string(int status);
 
 /* splitzip_compress for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc.  The same launches as splitzip_compress, with the encoder's
- * workspace (per-tile escape counts and record staging slots) in the
- * library's own device array (about 4 MiB per GPU, kept until the process
- * ends) instead of the tail of d_out, so d_out only needs room for the
- * largest stream:
+ * hipMalloc.  The encoder's workspace (per-tile escape counts and record
+ * staging slots) is the library's own device array (about 4 MiB per GPU,
+ * kept until the process ends) instead of the tail of d_out.  Inputs of at
+ * most 512 tiles (4M BF16 or 8M E5M2 elements) take one launch whose
+ * workgroups exchange their tiles' escape counts through that array (a wait
+ * for a count is bounded: SPLITZIP_STATIC_WAIT_POLLS polls, 64 if unset,
+ * after which the count is computed from the input); larger ones take the
+ * launches of splitzip_compress.  d_out only needs room for the largest
+ * stream:
  *   out_capacity >= A(P + 3 n_elems), P as in the layout above with
  *   n_elems escapes (splitzip_max_compressed_size minus the workspace).
  * Limit: n_elems <= 2048 * 8192 (BF16) or 2048 * 16384 (E5M2), 32 MiB of
@@ -164,7 +168,8 @@ const char* splitzip_status_string(int status);
  * synchronization, so it can be captured in a HIP graph.  Every call on one
  * GPU shares that GPU's workspace: calls that overlap on one GPU (two
  * streams, two host threads) race and may write wrong streams; serialize
- * them.  The stream passed must belong to the current device.
+ * them.  Calls that follow a race are not affected by it.  The stream
+ * passed must belong to the current device.
  * Returns SPLITZIP_OK, SPLITZIP_E_INVALID, SPLITZIP_E_CODEBOOK,
  * SPLITZIP_E_CAPACITY, SPLITZIP_E_TOO_LARGE or SPLITZIP_E_HIP. */
 int splitzip_compress_static(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks,

@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -305,7 +306,9 @@ struct EncArgs {
   uint32_t cb_args;       // codebooks read from prep.cbs (all of them fit), else from the stream
   uint32_t prep_in;       // header, codebooks and padding written by: 0 prep_kernel, 1 encode_sums, 2 encode_place
   uint32_t sums_in_place; // at most 64 blocks: encode_place sums the lower tiles itself, encode_sums is not launched
-  PrepArgs prep;          // the header work folded into a later launch (prep_in 1 or 2)
+  uint32_t* single;       // encode_single: arrival counter and per-tile count words (static array)
+  uint32_t wait_polls;    // encode_single: polls for a lower tile's count before it is computed here
+  PrepArgs prep;          // the header work folded into a later launch (prep_in 1, 2 or 3)
 };
 
 constexpr uint32_t kBlockTiles = 64;  // tiles per block of the escape-count sums (a placement range lies inside one)
@@ -918,6 +921,49 @@ __device__ void write_records(const EncArgs& a, const uint32_t* rec, uint64_t d0
   }
 }
 
+// Tile tt, whose n_i escapes take stream indices [dest, dest + n_i), encoded
+// again without stores, its records written in element order through the
+// LDS window rec (kPlaceRecs records) as whole words.  The exponent table is
+// built for the tile's codebook unless table_cb already names it.
+template <bool kBf16, int kVariant>
+__device__ inline void reencode_records(const EncArgs& a, uint32_t* rec, EncShared& esh, uint64_t tt, uint32_t n_i,
+                                        uint64_t dest, uint64_t& table_cb, uint32_t tid) {
+  const uint64_t cbi = a.seg_chunks ? codebook_of_chunk(tt >> (kBf16 ? 3 : 2), a.seg_chunks) : 0;
+  const TileIn in = kBf16 ? load_tile_bf16(a, tt, tid) : load_tile_e5m2(a, tt, tid);
+  if (cbi != table_cb) {
+    build_table<kVariant>(a, esh, cbi, kBf16 ? 256u : 32u, tid);
+    table_cb = cbi;
+  }
+  const TileEsc r = kBf16 ? encode_tile_bf16<kVariant>(a, esh, tt, in, false, tid)
+                          : encode_tile_e5m2(a, esh, tt, in, false, tid);
+  if (kBf16) {
+    // one window per group: a group of 2048 elements holds at most
+    // kPlaceRecs records, and its records follow the lower groups'
+#pragma unroll 1
+    for (uint32_t g = 0, g_first = 0; g < 4; ++g) {
+      const uint32_t cnt = ((g < 2 ? r.g01 : r.g23) >> (16 * (g & 1))) & 0xFFFFu;  // the same in every thread
+      if (cnt) {
+        group_escapes_bf16(tt, r, in, g, g_first, tid,
+                           [&](uint32_t k, uint32_t pos, uint32_t val) { rec[k] = pos | (val << 16); });
+        __syncthreads();
+        write_records<kVariant>(a, rec, dest + g_first, cnt, tid);
+        __syncthreads();  // rec is reused
+      }
+      g_first += cnt;
+    }
+  } else {
+    for (uint32_t w0 = 0; w0 < n_i; w0 += kPlaceRecs) {  // one window per 2048 records
+      auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) {
+        if (k - w0 < kPlaceRecs) rec[k - w0] = pos | (val << 16);
+      };
+      window_escapes_e5m2(tt, r, in, w0, kPlaceRecs, tid, stage);
+      __syncthreads();
+      write_records<kVariant>(a, rec, dest + w0, std::min<uint32_t>(kPlaceRecs, n_i - w0), tid);
+      __syncthreads();  // rec and esh are reused
+    }
+  }
+}
+
 // LDS of place_range for ranges of up to kMax tiles.
 template <uint32_t kMax>
 struct PlaceLds {
@@ -1053,41 +1099,7 @@ __device__ void place_range(const EncArgs& a, PlaceLds<kMax>& sh, EncShared& esh
     if (n_i <= kSlot) continue;  // uniform
     uint32_t tid_i = tid;
     asm volatile("" : "+v"(tid_i));
-    const uint64_t tt = t0 + i;
-    const uint64_t cbi = a.seg_chunks ? codebook_of_chunk(tt >> (kBf16 ? 3 : 2), a.seg_chunks) : 0;
-    const TileIn in = kBf16 ? load_tile_bf16(a, tt, tid_i) : load_tile_e5m2(a, tt, tid_i);
-    if (cbi != table_cb) {
-      build_table<kVariant>(a, esh, cbi, kBf16 ? 256u : 32u, tid_i);
-      table_cb = cbi;
-    }
-    const TileEsc r = kBf16 ? encode_tile_bf16<kVariant>(a, esh, tt, in, false, tid_i)
-                            : encode_tile_e5m2(a, esh, tt, in, false, tid_i);
-    if (kBf16) {
-      // one window per group: a group of 2048 elements holds at most
-      // kPlaceRecs records, and its records follow the lower groups'
-#pragma unroll 1
-      for (uint32_t g = 0, g_first = 0; g < 4; ++g) {
-        const uint32_t cnt = ((g < 2 ? r.g01 : r.g23) >> (16 * (g & 1))) & 0xFFFFu;  // the same in every thread
-        if (cnt) {
-          group_escapes_bf16(tt, r, in, g, g_first, tid_i,
-                             [&](uint32_t k, uint32_t pos, uint32_t val) { sh.rec[k] = pos | (val << 16); });
-          __syncthreads();
-          write_records<kVariant>(a, sh.rec, base + sh.pre_all[i] + g_first, cnt, tid_i);
-          __syncthreads();  // sh.rec is reused
-        }
-        g_first += cnt;
-      }
-    } else {
-      for (uint32_t w0 = 0; w0 < n_i; w0 += kPlaceRecs) {  // one window per 2048 records
-        auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) {
-          if (k - w0 < kPlaceRecs) sh.rec[k - w0] = pos | (val << 16);
-        };
-        window_escapes_e5m2(tt, r, in, w0, kPlaceRecs, tid_i, stage);
-        __syncthreads();
-        write_records<kVariant>(a, sh.rec, base + sh.pre_all[i] + w0, std::min<uint32_t>(kPlaceRecs, n_i - w0), tid_i);
-        __syncthreads();  // sh.rec and esh are reused
-      }
-    }
+    reencode_records<kBf16, kVariant>(a, sh.rec, esh, t0 + i, n_i, base + sh.pre_all[i], table_cb, tid_i);
   }
 }
 
@@ -1152,7 +1164,10 @@ __global__ __launch_bounds__(kThreads) void encode_place_top8_kernel(EncArgs a) 
 // one GPU share the array, so they race.
 constexpr uint32_t kStaticMaxTiles = 2048;  // 16M BF16 or 32M E5M2 elements (32 MiB)
 constexpr uint32_t kStaticStageAt = kStaticMaxTiles;  // words: tile counts, then staging slots
-constexpr uint64_t kStaticWords = kStaticStageAt + (uint64_t)kStaticMaxTiles * stage_slot(kMain);
+constexpr uint32_t kSingleMaxTiles = 512;   // one launch up to 4M BF16 or 8M E5M2 elements (8 MiB)
+constexpr uint64_t kSingleAt = kStaticStageAt + (uint64_t)kStaticMaxTiles * stage_slot(kMain);
+constexpr uint32_t kSingleCounts = 64;      // encode_single's words: the arrival counter, then (a cache line on) the count words
+constexpr uint64_t kStaticWords = kSingleAt + kSingleCounts + kSingleMaxTiles;
 
 static_assert(kStaticMaxTiles <= 64 * kBlockTiles, "inputs within the limit take the path without block sums");
 
@@ -1160,6 +1175,144 @@ static_assert(kStaticMaxTiles <= 64 * kBlockTiles, "inputs within the limit take
 // 4 MiB).  Host code reaches it only through the address hipGetSymbolAddress
 // returns with that GPU current.
 static __device__ __align__(256) uint32_t scratch[kStaticWords];
+
+// ------------------------------------------------- one-launch static encode
+//
+// Inputs of at most kSingleMaxTiles tiles take one launch in
+// splitzip_compress_static: each workgroup encodes its tile, publishes the
+// tile's escape count in the static array, adds up the counts of the lower
+// tiles and writes its own records at their place.  No escape record crosses
+// workgroups, only the count words, which are written and read with relaxed
+// device-scope atomics (coherent across the XCDs' L2 caches).  A count word
+// is valid | epoch << 16 | count.  The epoch is what a call-wide counter A
+// (static array) held when the workgroup started; every workgroup adds 1 to A
+// after publishing.  Calls on one stream run one after another, so every
+// workgroup of a call reads A at or above the value the previous call's
+// last workgroup left, which exceeds every epoch that call used (by less
+// than 2^15, the epoch's width): a word left by the previous call never
+// passes for this one.  A call also zeroes the count words of the tiles it
+// does not have, so no word outlives the call after the one that wrote it.
+// Nothing decides a "last" workgroup, so overlapping calls (which race, as
+// documented) leave no state that could mislead later calls.
+// A workgroup polls for a lower tile's count at most wait_polls times; a
+// count still missing then (its workgroup has not run yet, or started after
+// others of the call had finished and so read another epoch) is computed
+// from that tile's input, encoded again without stores.  No result depends
+// on the order the workgroups run in, and no wave waits without bound.
+constexpr uint32_t kCountValid = 1u << 31, kEpochShift = 16, kEpochMask = 0x7FFFu, kCountMask = 0xFFFFu;
+
+__device__ inline uint32_t load_agent(uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct SingleLds {
+  alignas(16) uint32_t rec[kPlaceRecs];       // the tile's records (position | exponent << 16) in element order
+  uint32_t missing[kSingleMaxTiles / 32];     // lower tiles whose count did not arrive in time
+  uint32_t epoch;
+};
+
+template <bool kBf16>
+__device__ void encode_single(const EncArgs& a) {
+  __shared__ EncShared sh;
+  __shared__ DenseLds<kBf16> dl;
+  __shared__ SingleLds ss;
+  const uint64_t n_tiles = a.n_tiles;
+  if (blockIdx.x == n_tiles) {  // the launch's extra workgroup: header, codebooks, padding
+    prep_work(a.prep, 0, 1);
+    return;
+  }
+  constexpr uint32_t kTpcLog2 = kBf16 ? 3 : 2;  // tiles per chunk: 8 BF16, 4 E5M2
+  constexpr uint32_t kPer = kSingleMaxTiles / kThreads;
+  const uint32_t tid = threadIdx.x;
+  const uint64_t t = blockIdx.x;
+  uint32_t* arrivals = a.single;  // A: workgroups that published, over all calls
+  uint32_t* counts = a.single + kSingleCounts;
+  if (tid == 0) ss.epoch = load_agent(arrivals) & kEpochMask;
+  if (tid < kSingleMaxTiles / 32) ss.missing[tid] = 0;
+  const TileIn in = kBf16 ? load_tile_bf16(a, t) : load_tile_e5m2(a, t);
+  build_table<kMain>(a, sh, a.seg_chunks ? codebook_of_chunk(t >> kTpcLog2, a.seg_chunks) : 0, kBf16 ? 256u : 32u);
+  uint4* escw = reinterpret_cast<uint4*>(dl.exps);
+  const TileEsc r = kBf16 ? encode_tile_bf16<kMain>(a, sh, t, in, true, tid, dl.exps)
+                          : encode_tile_e5m2(a, sh, t, in, true, tid, escw);
+  // publish (ss.epoch is visible: the table build and the rank scan hold barriers)
+  const uint32_t tag = kCountValid | (ss.epoch << kEpochShift);
+  if (tid == 0) {
+    store_agent(counts + t, tag | r.agg);
+    __hip_atomic_fetch_add(arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const bool staged = r.agg <= kPlaceRecs;  // uniform
+  if (staged) {
+    auto stage = [&](uint32_t k, uint32_t pos, uint32_t val) { ss.rec[k] = pos | (val << 16); };
+    if (kBf16) dense_escapes_bf16(t, r, dl.exps, stage);
+    else dense_escapes_e5m2(a, t, r, escw, stage);
+  }
+
+  // counts of the lower tiles: thread i awaits tiles i, i + 256, ...
+  uint32_t lower = 0, want = 0;
+#pragma unroll
+  for (uint32_t k = 0; k < kPer; ++k)
+    if (tid + k * kThreads < t) want |= 1u << k;
+  for (uint32_t p = 0;; ++p) {
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+      if (!((want >> k) & 1u)) continue;
+      const uint32_t w = load_agent(counts + tid + k * kThreads);
+      if ((w & ~kCountMask) == tag) {
+        lower += w & kCountMask;
+        want &= ~(1u << k);
+      }
+    }
+    if (!__syncthreads_or(want != 0) || p >= a.wait_polls) break;  // uniform
+    __builtin_amdgcn_s_sleep(2);
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < kPer; ++k) {
+    const uint32_t j = tid + k * kThreads;
+    if ((want >> k) & 1u) atomicOr(&ss.missing[j >> 5], 1u << (j & 31));
+  }
+  if (__syncthreads_or(want != 0)) {  // uniform: counts that never arrived, from the tiles' input
+    uint64_t table_cb = ~0ull;
+    for (uint32_t j = 0; j < (uint32_t)t; ++j) {
+      if (!((ss.missing[j >> 5] >> (j & 31)) & 1u)) continue;  // uniform
+      const uint64_t cbi = a.seg_chunks ? codebook_of_chunk(j >> kTpcLog2, a.seg_chunks) : 0;
+      const TileIn inj = kBf16 ? load_tile_bf16(a, j) : load_tile_e5m2(a, j);
+      if (cbi != table_cb) {
+        build_table<kMain>(a, sh, cbi, kBf16 ? 256u : 32u);
+        table_cb = cbi;
+      }
+      const TileEsc rj = kBf16 ? encode_tile_bf16<kMain>(a, sh, j, inj, false) : encode_tile_e5m2(a, sh, j, inj, false);
+      if (tid == 0) lower += rj.agg;
+    }
+  }
+  uint32_t base32 = 0;
+  block_exclusive_sum<kThreads / 64>(sh.red, lower, &base32);  // the total over the workgroup
+  const uint64_t base = base32;
+
+  if (tid == 0) {
+    if ((t & ((1u << kTpcLog2) - 1)) == 0) put_le(a.out + a.offsets + 8 * (t >> kTpcLog2), base, 8);
+    if (t == n_tiles - 1) {
+      const uint64_t e = base + r.agg, sz = a.esc + 3 * e;
+      put_le(a.out + a.offsets + 8 * a.chunks, e, 8);
+      put_le(a.out + 16, e, 8);
+      put_le(a.out + 24, sz, 8);
+      if (a.out_bytes) *a.out_bytes = sz;
+    }
+  }
+  if (staged) {
+    write_records<kMain>(a, ss.rec, base, r.agg);  // ss.rec is complete: the sums above hold barriers
+  } else {
+    uint64_t table_cb = ~0ull;  // the table may hold a lower tile's codebook
+    reencode_records<kBf16, kMain>(a, ss.rec, sh, t, r.agg, base, table_cb, tid);
+  }
+  // count words past this call's tiles, for the calls that follow
+  for (uint64_t j = n_tiles + t * kThreads + tid; j < kSingleMaxTiles; j += n_tiles * kThreads) store_agent(counts + j, 0);
+}
+
+__global__ __launch_bounds__(kThreads) void encode_single_bf16_kernel(EncArgs a) { encode_single<true>(a); }
+__global__ __launch_bounds__(kThreads) void encode_single_e5m2_kernel(EncArgs a) { encode_single<false>(a); }
 
 // ---------------------------------------------------------- decode kernels
 struct DecArgs {
@@ -2012,6 +2165,19 @@ size_t splitzip_max_compressed_size(int dtype, size_t n_elems, uint32_t n_codebo
 
 namespace {
 
+// Polls encode_single makes for a lower tile's count before computing it
+// itself: SPLITZIP_STATIC_WAIT_POLLS if set (0 makes every count that has not
+// arrived at the first poll be computed, which tests use), else 64 (about a
+// tenth of a millisecond; co-resident workgroups need one or two).
+uint32_t static_wait_polls() {
+  constexpr uint32_t kDefault = 64;
+  const char* v = getenv("SPLITZIP_STATIC_WAIT_POLLS");
+  if (v == nullptr || *v == 0) return kDefault;
+  char* end = nullptr;
+  const unsigned long x = strtoul(v, &end, 10);
+  return (end && *end == 0 && x <= 0xFFFFFFFFul) ? (uint32_t)x : kDefault;
+}
+
 // Host half of the compress entry points.  static_ws: the current device's
 // one-launch scratch (splitzip_compress_static), else nullptr (the workspace
 // is the tail of d_out).
@@ -2103,8 +2269,20 @@ int compress_impl(int dtype, int variant, const void* d_in, size_t n_elems, cons
   e.cb_args = cb_args;
   e.sums_in_place = blocks <= 64;
   e.prep_in = cb_args ? (e.sums_in_place ? 2 : 1) : 0;
+  e.single = nullptr;
+  e.wait_polls = 0;
   if (cb_args) prep_args(e.prep, 0);
   else memset(&e.prep, 0, sizeof(e.prep));
+  if (static_ws && variant == kMain && n_tiles <= kSingleMaxTiles) {
+    // one launch (encode_single), the header work as its extra workgroup
+    e.single = static_ws + kSingleAt;
+    e.wait_polls = static_wait_polls();
+    e.prep_in = cb_args ? 3 : 0;
+    const uint32_t wgs = tiles + (cb_args ? 1u : 0u);
+    if (dtype == SPLITZIP_FP8_E5M2) encode_single_e5m2_kernel<<<wgs, kThreads, 0, stream>>>(e);
+    else encode_single_bf16_kernel<<<wgs, kThreads, 0, stream>>>(e);
+    return hipGetLastError() == hipSuccess ? SPLITZIP_OK : SPLITZIP_E_HIP;
+  }
   if (dtype == SPLITZIP_FP8_E5M2) encode_dense_e5m2_kernel<<<tiles, kThreads, 0, stream>>>(e);
   else if (variant == kSentinel) encode_dense_sentinel_kernel<<<tiles, kThreads, 0, stream>>>(e);
   else if (variant == kTop8) encode_dense_top8_kernel<<<tiles, kThreads, 0, stream>>>(e);

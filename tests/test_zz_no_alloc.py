@@ -4,7 +4,18 @@ its stream equals splitzip_compress's byte for byte, on two calls in a row
 (the second with a smaller input), at the size limit, with escape-heavy tiles
 (placed by re-encoding), several and many codebooks, the exact minimum
 capacity, an empty input, and replayed from a HIP graph.  Sizes beyond its
-limit are refused before any GPU work."""
+limit are refused before any GPU work.
+
+Inputs of at most 512 tiles take one launch whose workgroups exchange escape
+counts through the static array (each count carries an epoch taken from a
+counter every workgroup advances, which keeps earlier calls' counts out):
+covered at the 512/513-tile boundary, over
+a run of calls whose sizes rise and fall (interleaved with the two-launch
+path), with codebooks that do not fit the kernel arguments, and with the
+counts computed from the input (SPLITZIP_STATIC_WAIT_POLLS=0, so no
+workgroup waits for another)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -143,3 +154,50 @@ def test_graph_replays_match_eager_calls():
         g.replay()
         torch.cuda.synchronize()
         assert int(nb.item()) == want.numel() and torch.equal(out[:want.numel()], want), f"replay {r}"
+
+
+def test_one_launch_boundary():
+    for dtype, tile, seed in ((kvsynth.BF16, 8192, 11), (kvsynth.E5M2, 16384, 12)):
+        x = kvsynth.random_bits(513 * tile, dtype, seed=seed, device=DEV, sigma=1.5)
+        cb = O.calibrate(dtype, kvsynth.to_numpy_bits(x[:100_000]))
+        _check(x[:512 * tile].contiguous(), cb, 0, f"512 tiles (one launch) dtype={dtype}")
+        _check(x, cb, 0, f"513 tiles (two launches) dtype={dtype}")
+        _check(x[:512 * tile - 5].contiguous(), cb, 0, f"512 tiles, ragged dtype={dtype}")
+
+
+def test_one_launch_sizes_rise_and_fall():
+    # count words of a larger earlier call must never pass for this call's
+    x = kvsynth.random_bits(1000 * 8192, kvsynth.BF16, seed=13, device=DEV, sigma=2.0)
+    cb = O.calibrate(O.BF16, kvsynth.to_numpy_bits(x[:100_000]))
+    for tiles in (500, 3, 500, 1, 512, 1000, 200, 37, 512, 2):
+        n = tiles * 8192 - (tiles % 3)
+        _check(x[:n].contiguous(), cb, 0, f"{tiles} tiles in a run of calls")
+
+
+def test_one_launch_codebooks_beyond_kernel_arguments():
+    # 201 codebooks for 10 chunks: the header launch of its own, then the one launch
+    x = kvsynth.random_bits(10 * 65536 - 9, kvsynth.BF16, seed=14, device=DEV, sigma=2.0)
+    rng = np.random.default_rng(14)
+    cbs = np.stack([rng.permutation(256)[:16] for _ in range(201)]).astype(np.uint8)
+    _check(x, cbs, 65536, "201 codebooks, 10 chunks")
+
+
+@pytest.mark.parametrize("case", ["bf16 per-layer", "bf16 escape-heavy", "e5m2 per-layer"])
+def test_one_launch_counts_computed_when_not_awaited(case):
+    old = os.environ.get("SPLITZIP_STATIC_WAIT_POLLS")
+    os.environ["SPLITZIP_STATIC_WAIT_POLLS"] = "0"
+    try:
+        if case == "bf16 per-layer":
+            wl, cbs = _layer("llama3_8b_kv_bf16", layers=4, tokens=128)  # 4 layers of 262,144: 128 tiles
+            _check(wl.data, cbs, wl.segment_elems, case)
+        elif case == "bf16 escape-heavy":
+            x = kvsynth.random_bits(40 * 8192 + 17, kvsynth.BF16, seed=15, device=DEV, kind="uniform_bits")
+            _check(x, O.calibrate(O.BF16, kvsynth.to_numpy_bits(x[:5000])), 0, case)
+        else:
+            wl, cbs = _layer("llama3_70b_kv_e5m2", layers=2, tokens=256)  # 2 layers of 524,288: 64 tiles
+            _check(wl.data, cbs, wl.segment_elems, case)
+    finally:
+        if old is None:
+            del os.environ["SPLITZIP_STATIC_WAIT_POLLS"]
+        else:
+            os.environ["SPLITZIP_STATIC_WAIT_POLLS"] = old
