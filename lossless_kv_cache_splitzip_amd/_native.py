@@ -349,7 +349,8 @@ def compress(x, codebooks, segment_elems: int = 0, out=None, out_bytes=None, str
 def compress_static(x, codebooks, segment_elems: int = 0, out=None, out_bytes=None, stream=None):
     """``compress`` through splitzip_compress_static: the encoder's
     workspace in the library's own device memory, for inputs of at most
-    2048 tiles (32 MiB).  Calls that overlap on one GPU race."""
+    2048 tiles (32 MiB); up to 512 tiles (8 MiB) in one launch.  Calls that
+    overlap on one GPU race."""
     import torch
     if not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous device tensor")
