@@ -3,7 +3,8 @@ for gfx950).  The encode and decode kernels are bound by their HBM streams
 and measured fastest with eight 256-thread workgroups per CU; fewer
 workgroups per CU, or register spills to scratch memory, cost them 1-10%.
 This test compiles the library's kernels the way the build does and fails
-if a streaming kernel needs scratch memory or falls below 8 waves per SIMD.
+if a streaming kernel needs scratch memory or falls below 8 waves per SIMD,
+or if any other kernel of the library spills to scratch memory.
 """
 import os
 import re
@@ -55,3 +56,14 @@ def test_streaming_kernels_keep_full_occupancy_and_no_scratch():
         print(kernel, r, flush=True)
         assert r.get("ScratchSize", 0) == 0, f"{kernel} spills to scratch: {r}"
         assert r.get("Occupancy") == 8, f"{kernel} runs below 8 waves per SIMD: {r}"
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_no_kernel_spills_to_scratch():
+    res = {}
+    for source in ("splitzip.hip", "calibrate.hip", "pipeline.hip", "copy_ceiling.hip"):
+        res.update(_resources(source))
+    assert len(res) >= 20, sorted(res)
+    assert any("encode_single_bf16_kernel" in k for k in res) and any("encode_single_e5m2_kernel" in k for k in res)
+    for kernel, r in res.items():
+        assert r.get("ScratchSize", 0) == 0, f"{kernel} spills to scratch: {r}"
