@@ -1929,9 +1929,10 @@ __global__ __launch_bounds__(kThreads) void decode_top8_kernel(DecArgs a) {
 #pragma unroll
     for (uint32_t g = 0; g < kGroups; ++g) {
       const uint8_t* c = code_t + g * 768 + ((3 * tid) & ~3u);
-      p0[g] = ld32(c);
-      p1[g] = ld32(c + 4);
-      sms[g] = *reinterpret_cast<const uint2*>(sm_t + g * 2048 + 8 * tid);
+      p0[g] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c));  // read once, as the codec's decoder
+      p1[g] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c + 4));
+      const u32x2_t s2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(sm_t + g * 2048 + 8 * tid));
+      sms[g] = make_uint2(s2.x, s2.y);
     }
   }
   const uint32_t l0 = ld32(cb), l1 = ld32(cb + 4);
@@ -2047,8 +2048,9 @@ __global__ __launch_bounds__(kThreads) void decode_sentinel_kernel(DecArgs a) {
     for (uint32_t g = 0; g < 4; ++g) {
       const uint32_t local = pfirst + g * 2048 + 8 * tid;
       if (full) {
-        nibs[g] = ld32(nib_c + local / 2);
-        sms[g] = *reinterpret_cast<const uint2*>(sm_c + local);
+        nibs[g] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(nib_c + local / 2));
+        const u32x2_t s2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(sm_c + local));  // read once
+        sms[g] = make_uint2(s2.x, s2.y);
       } else {
         const uint32_t valid = local < chunk_len ? std::min<uint32_t>(8, chunk_len - local) : 0u;
         uint32_t tn = 0, t0 = 0, t1 = 0;
