@@ -9,10 +9,10 @@ limit are refused before any GPU work.
 Inputs of at most 512 tiles take one launch whose workgroups exchange escape
 counts through the static array (each count carries an epoch taken from a
 counter every workgroup advances, which keeps earlier calls' counts out):
-covered at the 512/513-tile boundary, over
-a run of calls whose sizes rise and fall (interleaved with the two-launch
-path), with codebooks that do not fit the kernel arguments, and with the
-counts computed from the input (SPLITZIP_STATIC_WAIT_POLLS=0, so no
+covered at the 512/513-tile boundary, over a run of calls whose sizes rise
+and fall (interleaved with the two-launch path), over enough calls for the
+epoch to wrap, with codebooks that do not fit the kernel arguments, and with
+the counts computed from the input (SPLITZIP_STATIC_WAIT_POLLS=0, so no
 workgroup waits for another)."""
 import os
 
@@ -180,6 +180,26 @@ def test_one_launch_codebooks_beyond_kernel_arguments():
     rng = np.random.default_rng(14)
     cbs = np.stack([rng.permutation(256)[:16] for _ in range(201)]).astype(np.uint8)
     _check(x, cbs, 65536, "201 codebooks, 10 chunks")
+
+
+def test_one_launch_epoch_wraps():
+    # the epoch is the arrival counter modulo 2^15: about 45,000 tiles over
+    # 200 calls of cycling sizes cross the wrap at least once
+    x = kvsynth.random_bits(512 * 8192, kvsynth.BF16, seed=16, device=DEV, sigma=2.0)
+    cb = O.calibrate(O.BF16, kvsynth.to_numpy_bits(x[:100_000]))
+    sizes = [512, 1, 300, 17, 512, 64, 2, 400, 511, 33]
+    refs = {}
+    for tiles in sizes:
+        n = tiles * 8192 - (tiles % 5)
+        refs[tiles] = (x[:n].contiguous(), _reference(x[:n].contiguous(), cb, 0))
+    total = 0
+    for call in range(200):
+        tiles = sizes[call % len(sizes)]
+        xi, want = refs[tiles]
+        rc, out, nb = _static(xi, cb, 0)
+        assert rc == sz.OK and nb == want.numel() and torch.equal(out[:nb], want), f"call {call}: {tiles} tiles"
+        total += tiles
+    assert total > 2 ** 15
 
 
 @pytest.mark.parametrize("case", ["bf16 per-layer", "bf16 escape-heavy", "e5m2 per-layer"])
