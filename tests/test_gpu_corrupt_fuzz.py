@@ -198,3 +198,33 @@ def _check_codebook_cases(cases, dtype, n):
             rejected += 1
     print(f"  rejected {rejected}, still valid {accepted}", flush=True)
     assert rejected > 0 and accepted > 0
+
+
+@pytest.mark.parametrize("dtype", [O.BF16, O.E5M2], ids=["bf16", "e5m2"])
+@pytest.mark.parametrize("last", [10, 65536], ids=["short-last-chunk", "full-last-chunk"])
+def test_chunk_with_more_records_than_elements(dtype, last):
+    """Chunk offsets that give the last chunk more records than it has
+    elements (its start moved down into the previous chunk's records, E and S
+    unchanged) are rejected, as the oracle rejects them.  A chunk holds at
+    most one record per element; the decoder checks that bound before it
+    keeps a chunk's record count in 32 bits."""
+    n = 65536 + last
+    xh = kvsynth.to_numpy_bits(kvsynth.random_bits(n, dtype, seed=9, kind="uniform_bits"))
+    cb = O.calibrate(dtype, xh[:2000])
+    good = O.compress(dtype, xh, cb)
+    off1 = u64(good, 80 + 8)
+    cases = []
+    for k in (1, last + 1, 5000):
+        k = min(k, off1)
+        t = good.copy()
+        t[88:96] = np.frombuffer(np.uint64(off1 - k).tobytes(), np.uint8)
+        got_last = u64(t, 80 + 16) - u64(t, 88)
+        print(f"case more-records dtype={dtype} n={n} last chunk {last} elements, {got_last} records", flush=True)
+        cases.append((t, t.size, f"last chunk {got_last} records for {last} elements"))
+    assert any(u64(t, 80 + 16) - u64(t, 88) > last for t, _, _ in cases)
+    for t, in_bytes, label in cases:
+        want = O.validate(t, dtype, n)
+        assert want == O.E_CORRUPT, label
+        y, st = sz.decompress(torch.from_numpy(t).to(DEV), n, dtype, in_bytes=in_bytes)
+        torch.cuda.synchronize()
+        assert int(st.item()) == sz.E_CORRUPT, f"{label}: GPU status {int(st.item())}"
