@@ -310,10 +310,27 @@ def _dtype_of(t) -> int:
 
 
 def _stream_handle(stream) -> int:
+    """The HIP stream of `stream`, or torch's current stream on the current
+    device (through torch's raw-stream accessor when it has one: building a
+    Stream object costs more than the launch it is for)."""
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return int(stream.cuda_stream)
+    if stream is not None:
+        return int(stream.cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return int(raw(torch.cuda.current_device()))
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def _codebook_bytes(codebooks):
+    """(bytes, K) of K x 16 codebook entries.  The library reads them during
+    the call only, so a bytes copy is passed as the host pointer (cheaper than
+    a ctypes view of the array)."""
+    a = codebooks if type(codebooks) is np.ndarray and codebooks.dtype == np.uint8 else \
+        np.asarray(codebooks, dtype=np.uint8)
+    if a.size == 0 or a.size % 16:
+        raise ValueError(f"codebooks must hold K x 16 entries, got {a.size}")
+    return a.tobytes(), a.size // 16
 
 
 def compress(x, codebooks, segment_elems: int = 0, out=None, out_bytes=None, stream=None):
@@ -327,20 +344,19 @@ def compress(x, codebooks, segment_elems: int = 0, out=None, out_bytes=None, str
     if not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous device tensor")
     dtype = _dtype_of(x)
-    cbs = np.ascontiguousarray(np.asarray(codebooks, dtype=np.uint8)).reshape(-1, 16)
-    k = cbs.shape[0]
+    cbs, k = _codebook_bytes(codebooks)
     n = x.numel()
-    cap = splitzip_max_compressed_size(dtype, n, k)
-    if cap == 0:
-        raise SplitZipError(E_INVALID, "splitzip_max_compressed_size")
     if out is None:
+        cap = splitzip_max_compressed_size(dtype, n, k)
+        if cap == 0:
+            raise SplitZipError(E_INVALID, "splitzip_max_compressed_size")
         out = torch.empty(cap, dtype=torch.uint8, device=x.device)
     if out_bytes is None:
         out_bytes = torch.zeros(1, dtype=torch.int64, device=x.device)
     _device_buffer(out, "out", 0)  # its true size goes to the library, which checks the capacity
     _out_bytes_word(out_bytes)
-    rc = splitzip_compress(dtype, x.data_ptr(), n, cbs, k, segment_elems, out.data_ptr(), _nbytes(out),
-                           out_bytes.data_ptr(), _stream_handle(stream))
+    rc = load().splitzip_compress(dtype, x.data_ptr() or None, n, cbs, k, segment_elems, out.data_ptr(),
+                                  _nbytes(out), out_bytes.data_ptr(), _stream_handle(stream))
     if rc != OK:
         raise SplitZipError(rc, "splitzip_compress")
     return out, out_bytes
@@ -355,16 +371,15 @@ def compress_static(x, codebooks, segment_elems: int = 0, out=None, out_bytes=No
     if not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous device tensor")
     dtype = _dtype_of(x)
-    cbs = np.ascontiguousarray(np.asarray(codebooks, dtype=np.uint8)).reshape(-1, 16)
-    k = cbs.shape[0]
+    cbs, k = _codebook_bytes(codebooks)
     if out is None:  # room for the largest stream (and more: the workspace splitzip_compress needs)
         out = torch.empty(splitzip_max_compressed_size(dtype, x.numel(), k), dtype=torch.uint8, device=x.device)
     if out_bytes is None:
         out_bytes = torch.zeros(1, dtype=torch.int64, device=x.device)
     _device_buffer(out, "out", 0)  # the library checks the capacity
     _out_bytes_word(out_bytes)
-    rc = splitzip_compress_static(dtype, x.data_ptr(), x.numel(), cbs, k, segment_elems, out.data_ptr(),
-                                  _nbytes(out), out_bytes.data_ptr(), _stream_handle(stream))
+    rc = load().splitzip_compress_static(dtype, x.data_ptr() or None, x.numel(), cbs, k, segment_elems,
+                                         out.data_ptr(), _nbytes(out), out_bytes.data_ptr(), _stream_handle(stream))
     if rc != OK:
         raise SplitZipError(rc, "splitzip_compress_static")
     return out, out_bytes
@@ -389,8 +404,8 @@ def decompress(stream_buf, n_elems: int, dtype: int, out=None, status=None, in_b
     nbytes = _nbytes(stream_buf) if in_bytes is None else int(in_bytes)
     if nbytes > _nbytes(stream_buf):
         raise ValueError(f"in_bytes {nbytes} exceeds the stream buffer ({_nbytes(stream_buf)} bytes)")
-    rc = splitzip_decompress(stream_buf.data_ptr(), nbytes, dtype, n_elems, out.data_ptr(), status.data_ptr(),
-                             _stream_handle(stream))
+    rc = load().splitzip_decompress(stream_buf.data_ptr() or None, nbytes, dtype, n_elems, out.data_ptr() or None,
+                                    status.data_ptr(), _stream_handle(stream))
     if rc != OK:
         raise SplitZipError(rc, "splitzip_decompress")
     return out, status
