@@ -146,18 +146,17 @@ def variant_compress(variant: int, x, codebooks, segment_elems: int = 0, out=Non
     import torch
     if not x.is_cuda or not x.is_contiguous() or _dtype_of(x) != BF16:
         raise ValueError("x must be a contiguous BF16 device tensor")
-    cbs = np.ascontiguousarray(np.asarray(codebooks, dtype=np.uint8)).reshape(-1, 16)
-    k = cbs.shape[0]
-    cap = splitzip_variant_max_compressed_size(variant, x.numel(), k)
-    if cap == 0:
-        raise SplitZipError(E_INVALID, "splitzip_variant_max_compressed_size")
+    cbs, k = _codebook_bytes(codebooks)
     if out is None:
+        cap = splitzip_variant_max_compressed_size(variant, x.numel(), k)
+        if cap == 0:
+            raise SplitZipError(E_INVALID, "splitzip_variant_max_compressed_size")
         out = torch.empty(cap, dtype=torch.uint8, device=x.device)
     if out_bytes is None:
         out_bytes = torch.zeros(1, dtype=torch.int64, device=x.device)
     _device_buffer(out, "out", 0)  # its true size goes to the library, which checks the capacity
     _out_bytes_word(out_bytes)
-    rc = load().splitzip_variant_compress(variant, x.data_ptr(), x.numel(), cbs.ctypes.data, k, segment_elems,
+    rc = load().splitzip_variant_compress(variant, x.data_ptr() or None, x.numel(), cbs, k, segment_elems,
                                           out.data_ptr(), _nbytes(out), out_bytes.data_ptr(), _stream_handle(stream))
     if rc != OK:
         raise SplitZipError(rc, "splitzip_variant_compress")
