@@ -9,7 +9,10 @@
  *   - the decoded tensor equals the input byte for byte, with d_status OK;
  *   - a stream with a damaged magic number sets d_status to E_CORRUPT;
  *   - host-detectable errors (small output, null input, bad codebook) return
- *     their codes.
+ *     their codes;
+ *   - splitzip_compress_static, the entry point that allocates nothing,
+ *     writes the same stream byte for byte into a buffer with no room for a
+ *     workspace, on two calls in a row.
  * Then, on BF16 data, the other entry points from plain C: the device
  * calibration equals the host one, both ablation variants round-trip, and
  * the chunk-pipelined transfer through pinned host memory (four streams)
@@ -108,6 +111,41 @@ static void run(int dtype, size_t n) {
   uint8_t hdr[64];
   HIP(hipMemcpy(hdr, d_out, 64, hipMemcpyDeviceToHost));
   CHECK(rd64(hdr + 8) == n && rd64(hdr + 16) == E && rd64(hdr + 24) == S, "header n/E/S");
+
+  /* the same stream from the entry point that allocates nothing, into a
+   * buffer of exactly the largest stream's size (its workspace is the
+   * library's own), twice in a row */
+  {
+    const uint64_t C1 = (n + 65535) / 65536;
+    const uint64_t P = a256(64 + 16 + 8 * (C1 + 1)) + a256((n + 1) / 2) + a256(sm);
+    const size_t cap_s = (size_t)a256(P + 3 * (uint64_t)n);
+    void* d_s;
+    uint64_t* d_sbytes;
+    HIP(hipMalloc(&d_s, cap_s));
+    HIP(hipMalloc((void**)&d_sbytes, 8));
+    uint8_t* a = (uint8_t*)malloc(S);
+    uint8_t* b = (uint8_t*)malloc(S);
+    CHECK(a != NULL && b != NULL, "malloc");
+    HIP(hipMemcpy(a, d_out, S, hipMemcpyDeviceToHost));
+    for (int call = 0; call < 2; ++call) {
+      HIP(hipMemset(d_s, 0xA5, cap_s));
+      CHECK(splitzip_compress_static(dtype, d_in, n, cb, 1, 0, d_s, cap_s, d_sbytes, NULL) == SPLITZIP_OK,
+            "compress_static (call %d)", call);
+      uint64_t Ss = 0;
+      HIP(hipMemcpy(&Ss, d_sbytes, 8, hipMemcpyDeviceToHost));
+      CHECK(Ss == S, "static stream size %llu, splitzip_compress %llu", (unsigned long long)Ss,
+            (unsigned long long)S);
+      HIP(hipMemcpy(b, d_s, S, hipMemcpyDeviceToHost));
+      CHECK(memcmp(a, b, S) == 0, "static stream differs from splitzip_compress's (call %d)", call);
+    }
+    CHECK(splitzip_compress_static(dtype, d_in, n, cb, 1, 0, d_s, cap_s - 1, d_sbytes, NULL) ==
+              SPLITZIP_E_CAPACITY, "static: small output");
+    HIP(hipDeviceSynchronize());
+    free(a);
+    free(b);
+    HIP(hipFree(d_s));
+    HIP(hipFree(d_sbytes));
+  }
 
   CHECK(splitzip_decompress(d_out, S, dtype, n, d_y, d_status, NULL) == SPLITZIP_OK, "decompress");
   uint8_t* y = (uint8_t*)malloc(n * elem);

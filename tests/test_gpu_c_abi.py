@@ -1,9 +1,11 @@
 """The C ABI used from plain C (tests/c_abi/roundtrip.c, built by
 __graft_entry__.build()): hipMalloc'd buffers, the default stream, no Python
-or PyTorch in the process.  BF16 and E5M2 round trips, the closed-form stream
-size, the corrupt-stream status and host-detectable errors; then the device
-calibration against the host one, both ablation variants, and the
-chunk-pipelined transfer through pinned host memory on four streams."""
+or PyTorch in the process. BF16 and E5M2 round trips, the closed-form stream
+size, the corrupt-stream status and host-detectable errors, the stream of
+splitzip_compress_static (the entry point that allocates nothing) against
+splitzip_compress's; then the device calibration against the host one, both
+ablation variants, and the chunk-pipelined transfer through pinned host
+memory on four streams."""
 import os
 import subprocess
 
