@@ -5,8 +5,8 @@ no exponent split, no codebook, no escape logic.  Both the GPU path's tests and
 the CPU oracle's tests take their inputs from here.
 
 The SplitZip pages measure on KV activations of Qwen, Llama and Phi models and
-on "real BF16 activation tensors" (technical summary, Metodologia / Informacion
-Clave and Contribuciones Clave 2).  Those tensors are not available, so seeded
+on BF16 activations captured from real models (technical summary, Metodologia /
+Informacion Clave and Contribuciones Clave 2; the authors' abstract).  Those tensors are not available, so seeded
 synthetic tensors with the same layout and a similar exponent distribution
 stand in for them:
 
