@@ -182,7 +182,7 @@ int splitzip_compress_static(int dtype, const void* d_in, size_t n_elems, const 
  * of their own, to compare decode speed and size on this GPU:
  *   SPLITZIP_VARIANT_TOP15_SENTINEL  codebook entries 0..14 get codes 0..14;
  *     code 15 marks an escape, whose raw exponent is the next byte of the
- *     escape section (no positions: the pages' "saves metadata" design).
+ *     escape section (no positions: the pages' design with less side data).
  *   SPLITZIP_VARIANT_TOP8            codebook entries 0..7 get 3-bit codes,
  *     8 codes per 3 little-endian bytes (element j at bit 3j); escapes are the
  *     codec's 3-byte position records.
