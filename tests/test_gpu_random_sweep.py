@@ -1,0 +1,82 @@
+"""A seeded sweep of 120 random configurations through the GPU codec, each
+compared with the oracle: the stream byte for byte, the round trip bit for
+bit, and (inputs within its limit) splitzip_compress_static's stream against
+splitzip_compress's.  The configurations mix the two element types; sizes
+from empty to 9M elements, many of them a few elements either side of a
+tile, chunk or one-launch boundary; one codebook or several segments of whole
+chunks (some segments longer than needed, some codebooks unused); and data
+from narrow exponent distributions (few escapes) to uniformly random bit
+patterns (nearly every element escapes).  The codebooks are either calibrated
+on a sample of each segment or random valid ones.  Every case prints its
+parameters first, so a failure names it."""
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+sz = pytest.importorskip("lossless_kv_cache_splitzip_amd")
+DEV = "cuda"
+CASES = 120
+
+
+def _size(rng, dtype):
+    tile = 8192 if dtype == O.BF16 else 16384
+    pick = rng.integers(0, 6)
+    if pick == 0:
+        return int(rng.integers(0, 70_000))
+    if pick == 1:
+        return int(rng.integers(70_000, 3_000_000))
+    base = [tile, 65536, 512 * tile][pick - 2] if pick < 5 else 2048 * tile // 16
+    return max(0, int(base * rng.integers(1, 4) + rng.integers(-3, 4)))
+
+
+def _case(i):
+    rng = np.random.default_rng(10_000 + i)
+    dtype = O.BF16 if rng.integers(0, 3) else O.E5M2
+    n = min(_size(rng, dtype), 9_000_000)
+    chunks = max(1, -(-n // 65536))
+    if rng.integers(0, 3) == 0 or chunks == 1:
+        k, seg = 1, 0
+    else:
+        seg_chunks = int(rng.integers(1, chunks + 1))
+        seg = 65536 * seg_chunks
+        k = -(-max(n, 1) // seg) + int(rng.integers(0, 3))  # sometimes unused codebooks at the end
+    kind = "uniform_bits" if rng.integers(0, 8) == 0 else "gaussian"
+    sigma = float(rng.choice([0.3, 1.0, 2.0, 3.0]))
+    random_cb = bool(rng.integers(0, 4) == 0)
+    return rng, dtype, n, k, seg, kind, sigma, random_cb
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_random_configurations_match_the_oracle(chunk):
+    for i in range(chunk * CASES // 4, (chunk + 1) * CASES // 4):
+        rng, dtype, n, k, seg, kind, sigma, random_cb = _case(i)
+        print(f"case sweep {i}: dtype={dtype} n={n} K={k} segment={seg} kind={kind} sigma={sigma} "
+              f"random_codebooks={random_cb}", flush=True)
+        x = kvsynth.random_bits(n, dtype, seed=i, device=DEV, kind=kind, sigma=sigma)
+        xh = kvsynth.to_numpy_bits(x)
+        vals = 256 if dtype == O.BF16 else 32
+        if random_cb:
+            cbs = np.stack([rng.permutation(vals)[:16] for _ in range(k)]).astype(np.uint8)
+        else:
+            span = seg if k > 1 else max(n, 1)
+            cbs = np.stack([O.calibrate(dtype, xh[c * span:c * span + 4096]) for c in range(k)])
+        want = O.compress(dtype, xh, cbs, seg)
+        out, nb = sz.compress(x, cbs, seg)
+        torch.cuda.synchronize()
+        S = int(nb.item())
+        assert S == want.size, f"case {i}: stream size {S}, oracle {want.size}"
+        assert np.array_equal(out[:S].cpu().numpy(), want), f"case {i}: stream differs from the oracle's"
+        y, st = sz.decompress(out[:S], n, dtype)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0, f"case {i}: status {int(st.item())}"
+        assert np.array_equal(kvsynth.to_numpy_bits(y), xh), f"case {i}: round trip differs"
+        tile = 8192 if dtype == O.BF16 else 16384
+        if n <= 2048 * tile:
+            s_out, s_nb = sz.compress_static(x, cbs, seg)
+            torch.cuda.synchronize()
+            assert int(s_nb.item()) == S and torch.equal(s_out[:S], out[:S]), f"case {i}: static stream differs"
