@@ -1,6 +1,7 @@
 """A seeded sweep of 120 random configurations through the GPU codec, each
 compared with the oracle: the stream byte for byte, the round trip bit for
-bit, and (inputs within its limit) splitzip_compress_static's stream against
+bit, the on-device calibration of its segments against the host one, and
+(inputs within its limit) splitzip_compress_static's stream against
 splitzip_compress's.  The configurations mix the two element types; sizes
 from empty to 9M elements, many of them a few elements either side of a
 tile, chunk or one-launch boundary; one codebook or several segments of whole
@@ -75,6 +76,11 @@ def test_random_configurations_match_the_oracle(chunk):
         torch.cuda.synchronize()
         assert int(st.item()) == 0, f"case {i}: status {int(st.item())}"
         assert np.array_equal(kvsynth.to_numpy_bits(y), xh), f"case {i}: round trip differs"
+        # the on-device calibration of the same segments equals the host one
+        span = seg if k > 1 else max(n, 1)
+        dev_cbs = sz.calibrate_device(x, k, seg).cpu().numpy()
+        host_cbs = np.stack([O.calibrate(dtype, xh[c * span:(c + 1) * span]) for c in range(k)])
+        assert np.array_equal(dev_cbs, host_cbs), f"case {i}: device calibration differs"
         tile = 8192 if dtype == O.BF16 else 16384
         if n <= 2048 * tile:
             s_out, s_nb = sz.compress_static(x, cbs, seg)
