@@ -86,3 +86,32 @@ def test_random_configurations_match_the_oracle(chunk):
             s_out, s_nb = sz.compress_static(x, cbs, seg)
             torch.cuda.synchronize()
             assert int(s_nb.item()) == S and torch.equal(s_out[:S], out[:S]), f"case {i}: static stream differs"
+
+
+@pytest.mark.parametrize("variant", [O.SENTINEL, O.TOP8], ids=["sentinel", "top8"])
+def test_random_configurations_of_the_ablation_variants(variant):
+    """The same sweep's BF16 configurations (40 of them) through the two
+    ablation variants: stream byte for byte against the oracle's variant,
+    round trip bit for bit."""
+    done = 0
+    for i in range(CASES):
+        rng, dtype, n, k, seg, kind, sigma, random_cb = _case(i)
+        if dtype != O.BF16:
+            continue
+        print(f"case sweep variant={variant} {i}: n={n} K={k} segment={seg} kind={kind} sigma={sigma}", flush=True)
+        x = kvsynth.random_bits(n, O.BF16, seed=i, device=DEV, kind=kind, sigma=sigma)
+        xh = kvsynth.to_numpy_bits(x)
+        span = seg if k > 1 else max(n, 1)
+        cbs = np.stack([O.calibrate(O.BF16, xh[c * span:c * span + 4096]) for c in range(k)])
+        want = O.variant_compress(variant, xh, cbs, seg)
+        out, nb = sz.variant_compress(variant, x, cbs, seg)
+        torch.cuda.synchronize()
+        S = int(nb.item())
+        assert S == want.size and np.array_equal(out[:S].cpu().numpy(), want), f"case {i}: variant stream differs"
+        y, st = sz.variant_decompress(variant, out[:S], n)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0 and np.array_equal(kvsynth.to_numpy_bits(y), xh), f"case {i}: round trip"
+        done += 1
+        if done == 40:
+            break
+    assert done == 40
