@@ -19,7 +19,9 @@
  *     waited for.  Host-detectable argument errors return at once and enqueue
  *     nothing.  A failed kernel launch returns SPLITZIP_E_HIP.
  *   - Calls on different streams may run concurrently when their buffers are
- *     disjoint; the library keeps no mutable global state.
+ *     disjoint; the library keeps no mutable global state, except the device
+ *     array behind splitzip_compress_static (whose calls must not overlap on
+ *     one GPU; see there).
  *   - The device calls (compress, decompress and their variants, the device
  *     calibration) only launch kernels on `stream`: no allocation, memset or
  *     synchronization, so they can be captured in a HIP graph and replayed.
@@ -193,8 +195,8 @@ int splitzip_compress_static(int dtype, const void* d_in, size_t n_elems, const 
  * The arguments, alignment, workspace and status conventions are those of
  * splitzip_max_compressed_size, splitzip_compress and splitzip_decompress,
  * except that the top-8 workspace stages up to 1024 escape records per
- * 8192-element tile (4 KiB more per tile than the codec's 512); dtype is
- * BF16.  An invalid variant returns 0 / SPLITZIP_E_INVALID. */
+ * 8192-element tile (4 KiB per tile, against 2 KiB for the codec's 512);
+ * dtype is BF16.  An invalid variant returns 0 / SPLITZIP_E_INVALID. */
 typedef enum { SPLITZIP_VARIANT_TOP15_SENTINEL = 1, SPLITZIP_VARIANT_TOP8 = 2 } splitzip_variant;
 
 size_t splitzip_variant_max_compressed_size(int variant, size_t n_elems, uint32_t n_codebooks);
