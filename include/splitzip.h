@@ -283,11 +283,10 @@ int splitzip_pipeline_sizes(int dtype, size_t n_elems, uint32_t n_codebooks, siz
  * then naps 20 us between polls; if no step can proceed for 60 s it returns
  * SPLITZIP_E_HIP.  The call creates 4 * depth HIP events (no timing) and
  * destroys them before it returns; it allocates no device or host buffer.
- * On an error return, work
- * already queued may still run; synchronize the streams before reusing the
- * buffers.  Returns
- * SPLITZIP_OK, SPLITZIP_E_INVALID, SPLITZIP_E_CAPACITY, SPLITZIP_E_CODEBOOK
- * or SPLITZIP_E_HIP. */
+ * On an error return, work already queued may still run; synchronize the
+ * streams before reusing the buffers.  Returns SPLITZIP_OK,
+ * SPLITZIP_E_INVALID, SPLITZIP_E_CAPACITY, SPLITZIP_E_CODEBOOK or
+ * SPLITZIP_E_HIP. */
 int splitzip_pipeline_transfer(int dtype, const void* d_in, size_t n_elems, const uint8_t* h_codebooks,
                                uint32_t n_codebooks, size_t segment_elems, size_t group_elems, uint32_t depth,
                                int compress, void* d_work, size_t d_work_bytes, void* h_link, size_t h_link_bytes,
