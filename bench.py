@@ -407,7 +407,38 @@ def per_layer_graph_leg(reps: int = 50):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e3
 
+    def host_us(f, calls: int = 200):
+        """Host time per call, nothing synchronized inside the loop."""
+        import time as _t
+        f()
+        torch.cuda.synchronize()
+        t0 = _t.perf_counter()
+        for _ in range(calls):
+            f()
+        t1 = _t.perf_counter()
+        torch.cuda.synchronize()
+        return (t1 - t0) / calls * 1e6
+
+    lib = sz.load()
+    s0 = torch.cuda.current_stream().cuda_stream
+    cb_bytes = np.ascontiguousarray(cbs, dtype=np.uint8).tobytes()
+    S = int(nb.item())
+    host = {
+        "python_compress": host_us(lambda: sz.compress(wl.data, cbs, out=out, out_bytes=nb)),
+        "python_compress_static": host_us(lambda: sz.compress_static(wl.data, cbs, out=out_s, out_bytes=nb_s)),
+        "python_decompress": host_us(lambda: sz.decompress(out, wl.n, d, out=y, status=st, in_bytes=cap)),
+        "c_compress": host_us(lambda: lib.splitzip_compress(d, wl.data.data_ptr(), wl.n, cb_bytes, 1, 0,
+                                                            out.data_ptr(), cap, nb.data_ptr(), s0)),
+        "c_compress_static": host_us(lambda: lib.splitzip_compress_static(d, wl.data.data_ptr(), wl.n, cb_bytes, 1, 0,
+                                                                          out_s.data_ptr(), cap, nb_s.data_ptr(), s0)),
+        "c_decompress": host_us(lambda: lib.splitzip_decompress(out.data_ptr(), S, d, wl.n, y.data_ptr(),
+                                                                st.data_ptr(), s0)),
+    }
+
     res = {"workload": "kv_layer_bf16", "raw_bytes": wl.raw_bytes, "calls": reps,
+           # host time per call without synchronization: eager calls through the
+           # Python binding are partly host-bound
+           "host_us_per_call": host,
            "eager_encode_us": per_call_us(enc), "eager_decode_us": per_call_us(dec),
            "graph_encode_us": per_call_us(graphs["enc"].replay), "graph_decode_us": per_call_us(graphs["dec"].replay),
            # splitzip_compress_static: one launch, workspace in the library's own memory
