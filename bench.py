@@ -591,7 +591,7 @@ def main():
     ap.add_argument("--workload", default="llama3_8b_kv_bf16")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1),
-                    help="host threads of the parallel oracle run (the box grants 16)")
+                    help="host threads of the parallel oracle run (at most 16 by default)")
     ap.add_argument("--no-link", action="store_true", help="skip the pipelined host-link transfer leg")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the one-layer graph leg (its calls launch the same kernels on a 4 MiB input)")
