@@ -98,6 +98,15 @@ def status_string(status: int) -> str:
 
 
 # ------------------------------------------------------------ raw C-ABI calls
+def _host_codebooks(h_codebooks, n_codebooks: int) -> np.ndarray:
+    """The codebooks as contiguous bytes, at least 16 per codebook (the
+    library reads n_codebooks x 16 bytes through the pointer)."""
+    cbs = np.ascontiguousarray(h_codebooks, dtype=np.uint8)
+    if cbs.size < 16 * n_codebooks:
+        raise ValueError(f"h_codebooks holds {cbs.size} bytes, {16 * n_codebooks} needed for {n_codebooks} codebooks")
+    return cbs
+
+
 def splitzip_calibrate(dtype: int, host_samples) -> np.ndarray:
     """Top-16 exponent codebook of host samples (numpy or CPU tensor bits)."""
     a = _host_bits(host_samples, dtype)
@@ -115,7 +124,7 @@ def splitzip_max_compressed_size(dtype: int, n_elems: int, n_codebooks: int) -> 
 def splitzip_compress(dtype: int, d_in: int, n_elems: int, h_codebooks: np.ndarray, n_codebooks: int,
                       segment_elems: int, d_out: int, out_capacity: int, d_out_bytes: int | None,
                       stream: int | None) -> int:
-    cbs = np.ascontiguousarray(h_codebooks, dtype=np.uint8)
+    cbs = _host_codebooks(h_codebooks, n_codebooks)
     return int(load().splitzip_compress(dtype, d_in or None, n_elems, cbs.ctypes.data, n_codebooks,
                                         segment_elems, d_out or None, out_capacity, d_out_bytes or None,
                                         stream or None))
@@ -124,7 +133,7 @@ def splitzip_compress(dtype: int, d_in: int, n_elems: int, h_codebooks: np.ndarr
 def splitzip_compress_static(dtype: int, d_in: int, n_elems: int, h_codebooks: np.ndarray, n_codebooks: int,
                              segment_elems: int, d_out: int, out_capacity: int, d_out_bytes: int | None,
                              stream: int | None) -> int:
-    cbs = np.ascontiguousarray(h_codebooks, dtype=np.uint8)
+    cbs = _host_codebooks(h_codebooks, n_codebooks)
     return int(load().splitzip_compress_static(dtype, d_in or None, n_elems, cbs.ctypes.data, n_codebooks,
                                                segment_elems, d_out or None, out_capacity, d_out_bytes or None,
                                                stream or None))
@@ -235,9 +244,15 @@ def splitzip_pipeline_transfer(dtype: int, d_in: int, n_elems: int, h_codebooks:
                                segment_elems: int, group_elems: int, depth: int, compress: bool, d_work: int,
                                work_bytes: int, h_link: int, link_bytes: int, d_out: int, d_status: int | None,
                                h_group_bytes: np.ndarray | None, streams) -> int:
-    cbs = np.ascontiguousarray(h_codebooks, dtype=np.uint8)
+    cbs = _host_codebooks(h_codebooks, n_codebooks)
     arr = (ctypes.c_void_p * 4)(*[int(s) for s in streams])
-    gb = None if h_group_bytes is None else h_group_bytes.ctypes.data
+    gb = None
+    if h_group_bytes is not None:  # the library writes one u64 per group through it
+        groups = -(-n_elems // group_elems) if group_elems > 0 else 0
+        if (not isinstance(h_group_bytes, np.ndarray) or h_group_bytes.dtype != np.uint64
+                or not h_group_bytes.flags.c_contiguous or h_group_bytes.size < groups):
+            raise ValueError(f"h_group_bytes must be a contiguous uint64 array of at least {groups} entries")
+        gb = h_group_bytes.ctypes.data
     return int(load().splitzip_pipeline_transfer(dtype, d_in or None, n_elems, cbs.ctypes.data, n_codebooks,
                                                  segment_elems, group_elems, depth, int(bool(compress)),
                                                  d_work or None, work_bytes, h_link or None, link_bytes,

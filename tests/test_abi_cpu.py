@@ -162,3 +162,20 @@ def test_variant_max_size_and_argument_errors():
     assert lib.splitzip_variant_compress(2, p, 100, dup.ctypes.data, 1, 0, p, 1 << 20, None, None) == sz.E_CODEBOOK
     assert lib.splitzip_variant_decompress(0, p, 4096, 100, p, None, None) == sz.E_INVALID
     assert lib.splitzip_variant_decompress(1, p, 32, 100, p, None, None) == sz.E_INVALID   # shorter than a header
+
+
+def test_raw_wrappers_refuse_short_host_arrays():
+    # the library would read 16 x n_codebooks bytes, or write one u64 per
+    # group, through these pointers: the wrappers refuse arrays that are too short
+    fake = 1 << 20
+    cb = np.arange(16, dtype=np.uint8)
+    with pytest.raises(ValueError):
+        sz.splitzip_compress(O.BF16, fake, 10, cb, 2, 65536, fake, 1 << 30, None, None)
+    with pytest.raises(ValueError):
+        sz.splitzip_compress_static(O.BF16, fake, 10, cb[:8], 1, 0, fake, 1 << 30, None, None)
+    with pytest.raises(ValueError):
+        sz._native.splitzip_pipeline_transfer(O.BF16, fake, 3 * 65536, cb, 1, 0, 65536, 2, True, fake, 1 << 20,
+                                              fake, 1 << 20, fake, None, np.zeros(2, np.uint64), [0, 0, 0, 0])
+    with pytest.raises(ValueError):
+        sz._native.splitzip_pipeline_transfer(O.BF16, fake, 3 * 65536, cb, 1, 0, 65536, 2, True, fake, 1 << 20,
+                                              fake, 1 << 20, fake, None, np.zeros(3, np.int64), [0, 0, 0, 0])
