@@ -206,9 +206,11 @@ def cpu_baseline(wl, cbs, budget_s: float, threads: int):
 
 def link_leg(wl, cbs, seg, dtype, reps: int = 3):
     """The pages' transfer setting on one GPU: the workload moves through
-    pinned host memory over PCIe in groups of 16 MiB of raw data, up to
-    4 groups in flight, once raw and once compressed (compress -> copy to
-    host -> copy back -> decompress, copies by the copy engines).  Wall time of the blocking
+    pinned host memory over PCIe in groups of 32 MiB of raw data (one layer
+    of the 1 GiB cache; 4 to 128 MiB and depths 3 to 8 measured, 32 MiB at
+    depth 4 fastest), up to 4 groups in flight, once raw and once compressed
+    (compress -> copy to host -> copy back -> decompress, copies by the copy
+    engines).  Wall time of the blocking
     pipelined call, best of `reps` after one warm-up each.  As context, the
     copy engines moving the whole tensor to host and back at once."""
     import torch
@@ -216,7 +218,7 @@ def link_leg(wl, cbs, seg, dtype, reps: int = 3):
     import lossless_kv_cache_splitzip_amd as sz
 
     elem = wl.data.element_size()
-    group = (16 << 20) // elem
+    group = (32 << 20) // elem
     if seg and seg % group and group % seg:
         group = seg
     out = torch.empty_like(wl.data)
