@@ -108,5 +108,6 @@ def test_pipeline_escape_heavy_group():
 
 
 def test_pipeline_full_size_launch_configuration():
-    # the 1 GiB workload in the configuration the benchmark times
-    _run("llama3_8b_kv_bf16", 64 * CHUNK, 4)
+    # the 1 GiB workload in the configuration the benchmark times: groups of
+    # 32 MiB (one layer, 256 chunks), four in flight
+    _run("llama3_8b_kv_bf16", 256 * CHUNK, 4)
