@@ -30,6 +30,11 @@
 //                 moved to their place four at a time as whole words; tiles
 //                 whose records overflowed their slot are encoded again and
 //                 written through an LDS window.
+//   encode_single splitzip_compress_static up to 512 tiles, one launch:
+//                 each workgroup encodes its tile, publishes its escape
+//                 count in the library's static array, adds up the lower
+//                 tiles' counts (computing any that do not arrive in time)
+//                 and writes its own records.
 //   decode        one workgroup per tile inside one chunk (8192 BF16 or
 //                 16384 E5M2 elements).  A short chunk's escape records (in
 //                 groups of four, as words), then the dense data, are loaded
@@ -38,6 +43,8 @@
 //                 records; codes go through an LDS table
 //                 indexed by a whole nibble byte, and escapes are patched in
 //                 registers before non-temporal stores.
+//   *_sentinel_*, *_top8_*  the pages' two alternative designs (top-15 codes
+//                 with a sentinel; 3-bit top-8 codes), for comparison.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
